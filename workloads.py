@@ -1,0 +1,244 @@
+"""Seeded synthetic attention inputs, shared by the GPU path's tests/benchmark and by the oracle.
+
+This module only draws numbers and arranges them into tensors. It holds none of the
+attention arithmetic (no scores, no masking rule, no softmax): both sides of a parity
+check receive exactly the same stored values from here and compute on their own.
+
+Recipe (the same for every workload):
+  * ``numpy.random.Generator(PCG64(seed))``; draw order is q, k, v, then lengths, then mask.
+  * q/k/v are ``standard_normal(float32)`` values; 16-bit workloads round them to bf16/f16
+    by round-to-nearest-even through ``torch.Tensor.to``.  The device and the oracle consume
+    the same rounded values.
+  * KV-cache prefill: ``past[b] ~ U{0..max_past}`` (inclusive), ``total = past + Sq``;
+    K/V rows at or beyond ``total[b]`` are filled with NaN, so a kernel that reads and uses
+    them cannot match.
+  * Masked workload: an fp32 additive mask ``[B, Sq, Sk]`` with i.i.d. Bernoulli(p) entries set
+    to ``-inf`` (else ``0.0``), plus a few seeded query rows per batch set entirely to ``-inf``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+_TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass
+class Problem:
+    """One attention forward problem: host tensors plus the op's scalar arguments."""
+
+    name: str
+    q: torch.Tensor  # [B, H, Sq, D]
+    k: torch.Tensor  # [B, Hkv, C, D]
+    v: torch.Tensor  # [B, Hkv, C, D]
+    sk: int
+    causal: bool = False
+    local_window: int = 0
+    scale: float = 1.0
+    softcap: float = 0.0
+    mask: Optional[torch.Tensor] = None  # [planes, Sq, Sk]
+    total_lengths: Optional[torch.Tensor] = None  # int32 [B]
+    past_lengths: Optional[torch.Tensor] = None  # int32 [B]
+    out_layout: str = "head"  # "head" -> [B,H,Sq,D]; "token" -> [B,Sq,H*D]
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def kv_heads(self) -> int:
+        return self.k.shape[1]
+
+    @property
+    def sq(self) -> int:
+        return self.q.shape[2]
+
+    @property
+    def dim(self) -> int:
+        return self.q.shape[3]
+
+    @property
+    def kv_capacity(self) -> int:
+        return self.k.shape[2]
+
+    @property
+    def dtype(self) -> str:
+        return {v: k for k, v in _TORCH_DTYPES.items()}[self.q.dtype]
+
+    def kwargs(self) -> dict:
+        """Keyword arguments shared by the GPU binding and the oracle wrapper."""
+        return dict(
+            sk=self.sk,
+            mask=self.mask,
+            total_lengths=self.total_lengths,
+            past_lengths=self.past_lengths,
+            causal=self.causal,
+            local_window=self.local_window,
+            scale=self.scale,
+            softcap=self.softcap,
+            out_layout=self.out_layout,
+        )
+
+    def to(self, device) -> "Problem":
+        """A copy with every tensor moved to ``device``."""
+        moved = {}
+        for f in dataclasses.fields(self):
+            val = getattr(self, f.name)
+            moved[f.name] = val.to(device) if isinstance(val, torch.Tensor) else val
+        return Problem(**moved)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str, amp: float = 1.0) -> torch.Tensor:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if amp != 1.0:
+        x = x * np.float32(amp)
+    return torch.from_numpy(x).to(_TORCH_DTYPES[dtype])
+
+
+def make_problem(
+    *,
+    name: str = "custom",
+    seed: int,
+    batch: int,
+    heads: int,
+    kv_heads: int,
+    sq: int,
+    sk: int,
+    dim: int,
+    dtype: str,
+    kv_capacity: Optional[int] = None,
+    causal: bool = False,
+    local_window: int = 0,
+    scale: Optional[float] = None,
+    softcap: float = 0.0,
+    amp: float = 1.0,
+    lengths: Optional[str] = None,
+    max_past: int = 0,
+    nan_beyond_total: bool = False,
+    mask: Optional[str] = None,
+    mask_planes: Optional[int] = None,
+    mask_dtype: str = "f32",
+    mask_p: float = 0.1,
+    dead_rows: int = 0,
+    out_layout: str = "head",
+) -> Problem:
+    """Draw one problem.
+
+    ``lengths``: ``None`` (no length tensors), ``"past"`` (past ~ U{0..max_past}, total = past + sq),
+    ``"total"`` (only total_lengths ~ U{0..sk}) or ``"past_only"`` (only past_lengths).
+    ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0) or ``"normal"``
+    (finite N(0,1) values with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
+    ``dead_rows``: query rows per mask plane set entirely to -inf.
+    """
+    capacity = sk if kv_capacity is None else kv_capacity
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal(rng, (batch, heads, sq, dim), dtype, amp)
+    k = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp)
+    v = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp)
+
+    total = past = None
+    if lengths == "past":
+        past_np = rng.integers(0, max_past, size=batch, endpoint=True).astype(np.int32)
+        past = torch.from_numpy(past_np)
+        total = torch.from_numpy((past_np + np.int32(sq)).astype(np.int32))
+    elif lengths == "total":
+        total = torch.from_numpy(rng.integers(0, sk, size=batch, endpoint=True).astype(np.int32))
+    elif lengths == "past_only":
+        past = torch.from_numpy(rng.integers(0, max_past, size=batch, endpoint=True).astype(np.int32))
+    elif lengths is not None:
+        raise ValueError(f"unknown lengths recipe {lengths!r}")
+
+    if nan_beyond_total and total is not None:
+        for b in range(batch):
+            t = int(total[b])
+            if t < capacity:
+                k[b, :, t:, :] = float("nan")
+                v[b, :, t:, :] = float("nan")
+
+    mask_t = None
+    if mask is not None:
+        planes = batch if mask_planes is None else mask_planes
+        holes = rng.random(size=(planes, sq, sk), dtype=np.float32) < np.float32(mask_p)
+        if mask == "bernoulli":
+            m = np.zeros((planes, sq, sk), dtype=np.float32)
+        elif mask == "normal":
+            m = rng.standard_normal(size=(planes, sq, sk), dtype=np.float32)
+        else:
+            raise ValueError(f"unknown mask recipe {mask!r}")
+        m[holes] = -np.inf
+        del holes
+        if dead_rows:
+            for p in range(planes):
+                rows = rng.choice(sq, size=min(dead_rows, sq), replace=False)
+                m[p, rows, :] = -np.inf
+        mask_t = torch.from_numpy(m)
+        if mask_dtype != "f32":
+            mask_t = mask_t.to(_TORCH_DTYPES[mask_dtype])
+
+    return Problem(
+        name=name,
+        q=q,
+        k=k,
+        v=v,
+        sk=sk,
+        causal=causal,
+        local_window=local_window,
+        scale=(1.0 / math.sqrt(dim)) if scale is None else scale,
+        softcap=softcap,
+        mask=mask_t,
+        total_lengths=total,
+        past_lengths=past,
+        out_layout=out_layout,
+    )
+
+
+# The five named workloads at full size.  Seeds are the workload's ordinal (1..5).
+WORKLOADS = {
+    "tiny": dict(seed=1, batch=1, heads=1, kv_heads=1, sq=64, sk=64, dim=64, dtype="f32"),
+    "dit_joint": dict(
+        seed=2, batch=1, heads=24, kv_heads=24, sq=1536, sk=1536, dim=128, dtype="f32",
+        out_layout="token",
+    ),
+    "gqa_causal": dict(
+        seed=3, batch=4, heads=32, kv_heads=8, sq=2048, sk=2048, dim=128, dtype="bf16", causal=True,
+    ),
+    "kv_cache_prefill": dict(
+        seed=4, batch=8, heads=32, kv_heads=8, sq=512, sk=4096, kv_capacity=4096, dim=128,
+        dtype="f16", causal=True, local_window=1024, softcap=50.0, lengths="past", max_past=2048,
+        nan_beyond_total=True,
+    ),
+    "masked_long": dict(
+        seed=5, batch=2, heads=16, kv_heads=16, sq=4096, sk=4096, dim=64, dtype="bf16",
+        mask="bernoulli", mask_p=0.1, dead_rows=4,
+    ),
+}
+
+# Reduced copies with the same structure (dtype, features, GQA group, layout), small enough for
+# the full oracle to finish in seconds while still spanning several tiles and a ragged tail.
+SMALL_WORKLOADS = {
+    "tiny": dict(WORKLOADS["tiny"]),
+    "dit_joint": dict(WORKLOADS["dit_joint"], heads=3, sq=333, sk=333),
+    "gqa_causal": dict(WORKLOADS["gqa_causal"], batch=2, heads=8, kv_heads=2, sq=300, sk=300),
+    "kv_cache_prefill": dict(
+        WORKLOADS["kv_cache_prefill"], batch=3, heads=8, kv_heads=2, sq=77, sk=640, kv_capacity=640,
+        local_window=160, max_past=400,
+    ),
+    "masked_long": dict(WORKLOADS["masked_long"], heads=4, kv_heads=4, sq=261, sk=390),
+}
+
+
+def workload(name: str, small: bool = False, **overrides) -> Problem:
+    """The named workload (full size, or its reduced copy) with optional field overrides."""
+    table = SMALL_WORKLOADS if small else WORKLOADS
+    params = dict(table[name])
+    params.update(overrides)
+    return make_problem(name=name + ("_small" if small else ""), **params)
