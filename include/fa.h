@@ -1,0 +1,114 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) tiled online-softmax attention forward library (libfa.so).
+ *
+ * The operation is the prefill attention forward pass stated on the onnx-runtime-ep-cuda page
+ * `src/kernels/flash_attention.rs` (kernel argument list of `flash_attention_body`, host
+ * function `run`), with the token-major output of the pictor-kernels page
+ * `src/gpu_backend/cuda_imagen_attn_kernels.rs` (module documentation, "the op"):
+ *
+ *   for batch b, query head h, query row i:
+ *     kvh  = h / (heads / kv_heads)                      (consecutive heads share a KV head)
+ *     L    = total_lengths ? min(total_lengths[b], sk) : sk
+ *     cmax = past_lengths  ? past_lengths[b] + i : L - sq + i      (bottom-right causal)
+ *     lo   = local_window > 0 ? max(0, cmax + 1 - local_window) : 0
+ *     key j is attended iff j < L, (causal == 0 or j <= cmax) and j >= lo
+ *     x_j  = scale * <q[b,h,i,:], k[b,kvh,j,:]>
+ *            then, if softcap > 0:     x_j = softcap * tanh(x_j / softcap)
+ *            then, if mask_planes > 0: x_j += mask[plane, i, j]
+ *     out[b,h,i,:] = sum_j softmax_j(x) * v[b,kvh,j,:] over attended keys with x_j != -inf,
+ *                    or 0 when no such key exists.
+ *   plane = 0 when mask_planes == 1, b when mask_planes == batch, b*heads + h when
+ *   mask_planes == batch*heads (checked in that order).
+ *
+ * Threading and ownership: every pointer is caller-owned DEVICE memory, dense and contiguous
+ * in the layout stated per argument; the library never allocates, frees, copies to the host
+ * or synchronises on the call path and keeps no state between calls except the thread-local
+ * error text.  Work is enqueued on `stream` (a hipStream_t; NULL means the default stream)
+ * and the call returns before it runs.  `out` must not alias any input.  Device-side
+ * length values are not checked on the host (that would need a device-to-host copy); any
+ * int32 value is handled by the rule above.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  F16 is IEEE binary16, BF16 is bfloat16, both accumulated in fp32. */
+typedef enum fa_dtype { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2 } fa_dtype;
+
+/* Output layouts. */
+typedef enum fa_out_layout {
+    FA_OUT_HEAD_MAJOR = 0,  /* out [batch, heads, sq, dim]                                  */
+    FA_OUT_TOKEN_MAJOR = 1  /* out [batch, sq, heads*dim], out[b, i, h*dim + d]             */
+} fa_out_layout;
+
+/* Status codes. */
+enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARGUMENT = -1, /* inconsistent sizes, null required pointer, bad enum     */
+    FA_ERR_UNSUPPORTED = -2,      /* dtype, mask dtype or head dim outside what is built     */
+    FA_ERR_OVERFLOW = -3,         /* an element count, byte size or grid exceeds its range   */
+    FA_ERR_HIP = -4               /* the HIP runtime rejected the launch                     */
+};
+
+/*
+ * flash_attn_fwd — enqueue the attention forward pass described above.
+ *
+ *   q              [batch, heads, sq, dim] elements of `dtype`
+ *   k, v           [batch, kv_heads, kv_capacity, dim] elements of `dtype`; only rows j < L of
+ *                  each (b, kv head) plane are read (rows past L may hold anything, NaN included)
+ *   mask           NULL, or [mask_planes, sq, sk] elements of `mask_dtype` (row stride sk);
+ *                  -inf entries remove a key
+ *   total_lengths  NULL, or device int32[batch]: keys per batch entry (capped at sk)
+ *   past_lengths   NULL, or device int32[batch]: cache rows before this call's first query
+ *   out            output in `out_layout`, elements of `dtype`, rounded to nearest even
+ *   batch, sq, sk, kv_capacity >= 0; heads >= 0; kv_heads >= 1 and divides heads;
+ *   sk <= kv_capacity; 1 <= dim <= 128
+ *   causal         nonzero enables bottom-right aligned causal masking
+ *   mask_planes    0 (no mask), 1, batch or batch*heads; nonzero needs a non-NULL mask
+ *   local_window   <= 0 disables the window; otherwise keys j < cmax + 1 - local_window drop
+ *   scale          any finite value (typically 1/sqrt(dim))
+ *   softcap        <= 0 disables; otherwise finite
+ *   dtype          FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16
+ *   mask_dtype     FA_DTYPE_F32 or `dtype` (ignored without a mask)
+ *   out_layout     FA_OUT_HEAD_MAJOR or FA_OUT_TOKEN_MAJOR
+ *   stream         hipStream_t to enqueue on
+ *
+ * An empty problem (batch*heads*sq == 0) returns FA_OK without touching the device.  With
+ * sk == 0 (or every key removed) the output rows are written as 0.  On error nothing is
+ * enqueued (except FA_ERR_HIP, which reports a failed launch) and fa_last_error() describes
+ * the failure.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
+                   const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                   int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                   int causal, int mask_planes, int local_window, float scale, float softcap,
+                   int dtype, int mask_dtype, int out_layout, void* stream);
+
+/*
+ * fa_check_args — the argument validation flash_attn_fwd performs, without enqueuing
+ * anything or touching the HIP runtime.  Same arguments (minus the stream), same status
+ * codes.  Pointers are only checked for NULL where they are required.
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* mask,
+                  const int32_t* total_lengths, const int32_t* past_lengths, const void* out,
+                  int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                  int causal, int mask_planes, int local_window, float scale, float softcap,
+                  int dtype, int mask_dtype, int out_layout);
+
+/* Thread-local text describing the most recent non-FA_OK status on this thread ("" if none).
+ * The pointer stays valid until the next call into the library on the same thread. */
+const char* fa_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

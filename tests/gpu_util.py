@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and compare with the
+oracle on the same seeded inputs."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import tiled_online_softmax_flash_amd as fa
+
+# max-abs tolerances of the output vs the f64 oracle
+TOL = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+
+
+def say(msg: str) -> None:
+    """Name the GPU step about to run, unbuffered (survives a lost box)."""
+    print(msg, file=sys.__stderr__, flush=True)
+
+
+def run_gpu(prob, out_fill: float | None = None) -> torch.Tensor:
+    """The problem on cuda:0 through flash_attn_fwd; returns the output on the GPU."""
+    d = prob.to("cuda")
+    out = None
+    if out_fill is not None:
+        shape = (prob.batch, prob.heads, prob.sq, prob.dim) if prob.out_layout == "head" else (
+            prob.batch, prob.sq, prob.heads * prob.dim)
+        out = torch.full(shape, out_fill, dtype=prob.q.dtype, device="cuda")
+    res = fa.flash_attn_fwd(d.q, d.k, d.v, out=out, **d.kwargs())
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_full(prob) -> np.ndarray:
+    return oracle.forward(prob.q, prob.k, prob.v, **prob.kwargs())
+
+
+def oracle_rows(prob, rows) -> np.ndarray:
+    return oracle.rows(prob.q, prob.k, prob.v, rows, **prob.kwargs())
+
+
+def gpu_rows(out: torch.Tensor, prob, rows) -> np.ndarray:
+    """Rows (b, h, i) of a GPU output in either layout, as float64 [n, D]."""
+    D = prob.dim
+    host = out.double().cpu().numpy()
+    res = np.empty((len(rows), D))
+    for n, (b, h, i) in enumerate(rows):
+        if prob.out_layout == "head":
+            res[n] = host[b, h, i]
+        else:
+            res[n] = host[b, i, h * D:(h + 1) * D]
+    return res
+
+
+def check(got: np.ndarray, want: np.ndarray, dtype: str, name: str, amp: float = 1.0) -> dict:
+    """Max-abs gate at the dtype's tolerance.  Inputs scaled by ``amp`` move output values up by
+    at most ceil(log2(amp)) binades, which multiplies the 16-bit rounding error of P and of the
+    output by at most 2**ceil(log2(amp)); the gate scales by that factor."""
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = np.abs(got - want)
+    max_abs = float(err.max()) if err.size else 0.0
+    rel = float((err / np.maximum(np.abs(want), 1e-2)).max()) if err.size else 0.0
+    tol = TOL[dtype] * (2.0 ** math.ceil(math.log2(amp)) if amp > 1.0 else 1.0)
+    say(f"  {name}: max_abs={max_abs:.3e} max_rel(floor 1e-2)={rel:.3e} tol={tol:.0e}")
+    assert max_abs <= tol, f"{name}: max abs error {max_abs:.3e} > {tol:.0e}"
+    # rows the oracle returns as exactly zero (nothing attended) must be exactly zero
+    zero_rows = np.all(want == 0.0, axis=-1)
+    if zero_rows.any():
+        assert np.all(got[zero_rows] == 0.0), f"{name}: fully masked rows are not exactly 0"
+    return dict(max_abs=max_abs, max_rel=rel)
+
+
+def sample_rows(prob, n: int, seed: int = 1234, extra=()) -> list:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = set(tuple(int(x) for x in r) for r in extra)
+    B, H, Sq = prob.batch, prob.heads, prob.sq
+    for corner in [(0, 0, 0), (B - 1, H - 1, Sq - 1), (0, H - 1, Sq // 2), (B - 1, 0, Sq - 1)]:
+        rows.add(corner)
+    target = min(B * H * Sq, n + len(rows))
+    while len(rows) < target:
+        rows.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq))))
+    return sorted(rows)

@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point, and validates
+arguments (no kernel is launched; validation touches no HIP state)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import tiled_online_softmax_flash_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["fa_check_args", "fa_last_error", "fa_version", "flash_attn_fwd"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version():
+    assert fa.version() == "0.1.0"
+
+
+GOOD = dict(q=16, k=16, v=16, out=16, batch=2, heads=8, kv_heads=2, sq=100, sk=90,
+            kv_capacity=128, dim=64, causal=1, mask_planes=0, local_window=0, scale=0.125,
+            softcap=0.0, dtype=fa.FA_DTYPE_BF16, mask_dtype=fa.FA_DTYPE_F32, out_layout=0)
+
+
+def status(**over):
+    args = dict(GOOD)
+    args.update(over)
+    return fa.check_args(**args)
+
+
+def test_valid_arguments_pass():
+    assert status() == fa.FA_OK
+    assert status(dtype=fa.FA_DTYPE_F32) == fa.FA_OK
+    assert status(dtype=fa.FA_DTYPE_F16, out_layout=1) == fa.FA_OK
+    assert status(mask=16, mask_planes=2) == fa.FA_OK
+    assert status(mask=16, mask_planes=16, mask_dtype=fa.FA_DTYPE_BF16) == fa.FA_OK
+    assert status(mask=16, mask_planes=1) == fa.FA_OK
+    for d in (1, 7, 40, 80, 128):
+        assert status(dim=d) == fa.FA_OK, d
+    assert status(softcap=50.0, local_window=1024) == fa.FA_OK
+    assert status(scale=0.0) == fa.FA_OK and status(scale=-1.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dim=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(dim=129), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=16, mask_planes=2, mask_dtype=fa.FA_DTYPE_F16), fa.FA_ERR_UNSUPPORTED),
+    (dict(out_layout=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(sq=-5), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(kv_heads=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(heads=6, kv_heads=4), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(sk=129), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(mask=16, mask_planes=3), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(mask=None, mask_planes=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(mask=16, mask_planes=-2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(softcap=float("nan")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=2**30, heads=2**30, kv_heads=1), fa.FA_ERR_OVERFLOW),
+    (dict(batch=2**20, heads=2**16, kv_heads=1, sq=2**20, kv_capacity=1, sk=1, dim=128),
+     fa.FA_ERR_OVERFLOW),
+    (dict(mask=16, mask_planes=2**20, batch=2**20, heads=1, kv_heads=1, sq=2**20, sk=2**20,
+          kv_capacity=2**20), fa.FA_ERR_OVERFLOW),
+    (dict(batch=2**16, heads=2**16, kv_heads=1, sq=1, dim=1), fa.FA_ERR_OVERFLOW),
+])
+def test_invalid_arguments_are_rejected(over, code):
+    assert status(**over) == code
+    assert fa.last_error() != ""
+
+
+def test_empty_problems_are_ok_without_pointers():
+    assert status(batch=0, q=None, k=None, v=None, out=None) == fa.FA_OK
+    assert status(sq=0, q=None, out=None) == fa.FA_OK
+    assert status(heads=0, q=None, out=None) == fa.FA_OK
+    # no keys at all: k and v may be null, the rows are written as zeros
+    assert status(sk=0, kv_capacity=0, k=None, v=None) == fa.FA_OK
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 1, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, q, q)
+
+
+def test_binding_rejects_mismatched_shapes_and_dtypes():
+    q = torch.zeros(1, 2, 4, 8)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, torch.zeros(1, 2, 4, 16), torch.zeros(1, 2, 4, 16))
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, q.double(), q.double())

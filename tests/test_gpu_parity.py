@@ -1,0 +1,206 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the f64 oracle, element by element.
+
+Tolerance: max-abs 1e-4 for fp32 inputs and 2e-2 for bf16/f16 inputs (fp32 accumulation);
+rows with no attended finite key must be exactly 0.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_online_softmax_flash_amd as fa
+import workloads
+from gpu_util import (TOL, check, gpu_rows, oracle_full, oracle_rows, run_gpu, sample_rows, say)
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+NAMES = list(workloads.WORKLOADS)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_small_workload_full_output(name):
+    prob = workloads.workload(name, small=True)
+    say(f"[gpu] small workload {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} {prob.dtype}")
+    got = run_gpu(prob, out_fill=float("nan")).double().cpu().numpy()
+    want = oracle_full(prob)
+    check(got, want, prob.dtype, name)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_workload_sampled_rows(name):
+    prob = workloads.workload(name)
+    say(f"[gpu] full workload {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} {prob.dtype}")
+    out = run_gpu(prob, out_fill=float("nan"))
+    assert bool(torch.isfinite(out).all()), "non-finite values in the output"
+    extra = []
+    if prob.mask is not None:
+        dead = torch.nonzero(torch.isinf(prob.mask).all(dim=-1))  # (plane, i)
+        for plane, i in dead.tolist():
+            for h in (0, prob.heads - 1):
+                extra.append((plane, h, i))
+        # every (b, h) of a fully masked mask row is exactly zero
+        for plane, i in dead.tolist():
+            if prob.out_layout == "head":
+                assert bool((out[plane, :, i] == 0).all())
+    rows = sample_rows(prob, 384, extra=extra)
+    check(gpu_rows(out, prob, rows), oracle_rows(prob, rows), prob.dtype, name)
+
+
+# ------------------------------------------------------------------------------------------
+# edge cases of the key rule and the epilogue
+
+EDGE = {
+    "window_one_past": dict(seed=21, batch=3, heads=4, kv_heads=2, sq=70, sk=300, dim=64,
+                            dtype="bf16", causal=True, local_window=1, lengths="past",
+                            max_past=200),
+    "window_wider_than_keys": dict(seed=22, batch=2, heads=4, kv_heads=4, sq=130, sk=130, dim=64,
+                                   dtype="f16", causal=True, local_window=5000),
+    "past_zero_total_short": dict(seed=23, batch=2, heads=2, kv_heads=1, sq=200, sk=256,
+                                  dim=128, dtype="bf16", causal=True, lengths="past", max_past=0),
+    "queries_exceed_keys": dict(seed=24, batch=2, heads=2, kv_heads=2, sq=300, sk=70, dim=64,
+                                dtype="bf16", causal=True),
+    "total_only_random": dict(seed=25, batch=4, heads=2, kv_heads=1, sq=90, sk=333, dim=64,
+                              dtype="f16", lengths="total"),
+    "past_only": dict(seed=26, batch=3, heads=2, kv_heads=2, sq=65, sk=400, dim=64, dtype="bf16",
+                      causal=True, lengths="past_only", max_past=300),
+    "window_non_causal": dict(seed=27, batch=2, heads=2, kv_heads=1, sq=129, sk=260, dim=32,
+                              dtype="bf16", local_window=70),
+    "single_query_row": dict(seed=28, batch=2, heads=8, kv_heads=2, sq=1, sk=777, dim=128,
+                             dtype="bf16", causal=True),
+    "single_key": dict(seed=29, batch=1, heads=3, kv_heads=1, sq=40, sk=1, dim=64, dtype="f16"),
+    "softcap_saturating": dict(seed=30, batch=2, heads=4, kv_heads=2, sq=150, sk=200, dim=64,
+                               dtype="f16", softcap=2.0, amp=3.0, causal=True),
+    "softcap_huge_is_plain": dict(seed=31, batch=1, heads=2, kv_heads=1, sq=100, sk=100, dim=64,
+                                  dtype="bf16", softcap=1e30),
+    "softcap_with_mask": dict(seed=32, batch=2, heads=2, kv_heads=2, sq=100, sk=96, dim=64,
+                              dtype="bf16", softcap=5.0, mask="normal", mask_p=0.2),
+    "mask_single_plane": dict(seed=33, batch=2, heads=4, kv_heads=2, sq=77, sk=140, dim=64,
+                              dtype="bf16", mask="bernoulli", mask_planes=1, mask_p=0.3,
+                              dead_rows=2),
+    "mask_per_head": dict(seed=34, batch=2, heads=3, kv_heads=3, sq=70, sk=130, dim=64,
+                          dtype="f16", mask="normal", mask_planes=6, mask_p=0.1, dead_rows=1),
+    "mask_bf16_values": dict(seed=35, batch=2, heads=2, kv_heads=1, sq=66, sk=192, dim=128,
+                             dtype="bf16", mask="normal", mask_dtype="bf16", mask_p=0.1),
+    "mask_ragged_sk": dict(seed=36, batch=1, heads=2, kv_heads=2, sq=50, sk=131, dim=64,
+                           dtype="bf16", mask="normal", mask_p=0.1, causal=True),
+    "mask_with_lengths": dict(seed=37, batch=3, heads=2, kv_heads=1, sq=40, sk=300, dim=64,
+                              dtype="bf16", mask="bernoulli", mask_p=0.1, causal=True,
+                              local_window=100, lengths="past", max_past=200,
+                              nan_beyond_total=True),
+    "capacity_beyond_sk": dict(seed=38, batch=2, heads=4, kv_heads=2, sq=100, sk=150,
+                               kv_capacity=512, dim=128, dtype="bf16", causal=True),
+    "scale_negative": dict(seed=39, batch=1, heads=2, kv_heads=1, sq=80, sk=120, dim=64,
+                           dtype="bf16", scale=-0.2),
+    "scale_zero": dict(seed=40, batch=1, heads=2, kv_heads=1, sq=80, sk=120, dim=64,
+                       dtype="bf16", scale=0.0, causal=True),
+    "token_major_batched": dict(seed=41, batch=3, heads=5, kv_heads=5, sq=70, sk=90, dim=64,
+                                dtype="bf16", out_layout="token", causal=True),
+    "token_major_fp32": dict(seed=42, batch=2, heads=3, kv_heads=1, sq=100, sk=100, dim=128,
+                             dtype="f32", out_layout="token"),
+    "fp32_gqa_causal_window": dict(seed=43, batch=2, heads=4, kv_heads=2, sq=150, sk=180,
+                                   dim=64, dtype="f32", causal=True, local_window=50,
+                                   lengths="past", max_past=30),
+    "fp32_mask_softcap": dict(seed=44, batch=2, heads=2, kv_heads=2, sq=70, sk=100, dim=64,
+                              dtype="f32", mask="bernoulli", mask_p=0.2, dead_rows=3,
+                              softcap=3.0),
+    "amp3_bf16_causal": dict(seed=45, batch=1, heads=4, kv_heads=1, sq=300, sk=300, dim=128,
+                             dtype="bf16", causal=True, amp=3.0),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_case(name):
+    prob = workloads.make_problem(name=name, **EDGE[name])
+    say(f"[gpu] edge {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} sk={prob.sk} {prob.dtype}")
+    got = run_gpu(prob, out_fill=float("nan")).double().cpu().numpy()
+    check(got, oracle_full(prob), prob.dtype, name, amp=EDGE[name].get("amp", 1.0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dim", [1, 8, 40, 64, 72, 100, 128])
+def test_head_dims(dtype, dim):
+    prob = workloads.make_problem(name=f"dim{dim}", seed=50 + dim, batch=2, heads=4, kv_heads=2,
+                                  sq=133, sk=161, dim=dim, dtype=dtype, causal=True)
+    say(f"[gpu] head dim {dim} {dtype}")
+    got = run_gpu(prob, out_fill=float("nan")).double().cpu().numpy()
+    check(got, oracle_full(prob), dtype, f"dim{dim}-{dtype}")
+
+
+def test_f16_relative_error_across_amplitudes():
+    """Relative error with a floored denominator stays at the fp16 rounding floor at unit and
+    larger input magnitudes: the accumulators must be fp32.  This is the amplitude sweep of the
+    parity test on the onnx-runtime-ep-cuda page src/kernels/flash_attention.rs, with its
+    one-signed input range ([-1, 0) times the amplitude) and its gates (2e-3 absolute at unit
+    amplitude, 6e-3 relative with the denominator floored at 1e-2)."""
+    worst_rel = 0.0
+    for amp in (1.0, 3.0):
+        for seq in (2, 30, 64, 96, 192, 300):
+            prob = workloads.make_problem(name="amp", seed=60 + seq, batch=1, heads=14,
+                                          kv_heads=2, sq=seq, sk=seq, dim=64, dtype="f16",
+                                          causal=True, amp=amp, dist="neg_uniform")
+            say(f"[gpu] f16 amplitude {amp} seq {seq}")
+            got = run_gpu(prob).double().cpu().numpy()
+            want = oracle_full(prob)
+            err = np.abs(got - want)
+            worst_rel = max(worst_rel, float((err / np.maximum(np.abs(want), 1e-2)).max()))
+            if amp == 1.0:
+                assert err.max() < 2e-3
+    say(f"  worst relative error {worst_rel:.3e}")
+    assert worst_rel < 6e-3
+
+
+def test_no_keys_writes_zeros():
+    prob = workloads.make_problem(name="nokeys", seed=70, batch=2, heads=4, kv_heads=2, sq=50,
+                                  sk=0, kv_capacity=0, dim=64, dtype="bf16")
+    say("[gpu] sk = 0")
+    out = run_gpu(prob, out_fill=float("nan"))
+    assert bool((out == 0).all())
+
+
+def test_lengths_all_zero_writes_zeros():
+    prob = workloads.make_problem(name="zerolen", seed=71, batch=2, heads=2, kv_heads=2, sq=64,
+                                  sk=64, dim=64, dtype="f16")
+    prob.total_lengths = torch.zeros(2, dtype=torch.int32)
+    say("[gpu] total_lengths = 0")
+    out = run_gpu(prob, out_fill=float("nan"))
+    assert bool((out == 0).all())
+
+
+def test_empty_problem_is_a_no_op():
+    q = torch.empty(0, 4, 16, 64, dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    say("[gpu] empty batch")
+    out = fa.flash_attn_fwd(q, kv, kv)
+    assert out.shape == (0, 4, 16, 64)
+
+
+def test_side_stream_and_out_argument():
+    prob = workloads.workload("gqa_causal", small=True)
+    d = prob.to("cuda")
+    out = torch.full_like(d.q, float("nan"))
+    s = torch.cuda.Stream()
+    say("[gpu] side stream")
+    with torch.cuda.stream(s):
+        res = fa.flash_attn_fwd(d.q, d.k, d.v, out=out, **d.kwargs())
+    s.synchronize()
+    assert res.data_ptr() == out.data_ptr()
+    check(out.double().cpu().numpy(), oracle_full(prob), prob.dtype, "side-stream")
+
+
+def test_repeated_calls_are_deterministic():
+    prob = workloads.workload("masked_long", small=True)
+    say("[gpu] determinism")
+    a = run_gpu(prob)
+    b = run_gpu(prob)
+    assert torch.equal(a, b)
+
+
+def test_gpu_rejects_noncontiguous_input():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, q, q)

@@ -1,0 +1,164 @@
+"""MI355X (gfx950) tiled online-softmax attention forward.
+
+Python binding of ``libfa.so`` (C ABI in ``include/fa.h``).  It only marshals arguments:
+torch tensors supply device memory and the current HIP stream, and every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the library or a GPU
+is missing, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "flash_attn_fwd", "check_args", "last_error", "version", "FaError", "library_path",
+    "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_OVERFLOW", "FA_ERR_HIP",
+    "FA_DTYPE_F32", "FA_DTYPE_F16", "FA_DTYPE_BF16",
+]
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_OVERFLOW = -3
+FA_ERR_HIP = -4
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_F16 = 1
+FA_DTYPE_BF16 = 2
+
+_DTYPE_CODE = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+               torch.bfloat16: FA_DTYPE_BF16}
+_LAYOUT_CODE = {"head": 0, "token": 1}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libfa.so")
+
+_lib = None
+
+_ARGS = [
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q k v mask
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                   # total past out
+    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    ctypes.c_int,                                                         # B H Hkv Sq Sk C D
+    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+    ctypes.c_int, ctypes.c_int, ctypes.c_int,
+]
+
+
+class FaError(RuntimeError):
+    """A non-OK status from libfa.so, with the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"flash_attn_fwd failed with status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            from . import _build
+
+            _build.build()
+        lib = ctypes.CDLL(library_path)
+        lib.flash_attn_fwd.argtypes = _ARGS + [ctypes.c_void_p]
+        lib.flash_attn_fwd.restype = ctypes.c_int
+        lib.fa_check_args.argtypes = list(_ARGS)
+        lib.fa_check_args.restype = ctypes.c_int
+        lib.fa_last_error.argtypes = []
+        lib.fa_last_error.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return _load().fa_last_error().decode()
+
+
+def version() -> str:
+    return _load().fa_version().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def check_args(*, q=None, k=None, v=None, mask=None, total_lengths=None, past_lengths=None,
+               out=None, batch, heads, kv_heads, sq, sk, kv_capacity, dim, causal=0,
+               mask_planes=0, local_window=0, scale=1.0, softcap=0.0, dtype=FA_DTYPE_BF16,
+               mask_dtype=FA_DTYPE_F32, out_layout=0) -> int:
+    """The library's validation status for raw arguments (pointers are ints or None)."""
+    return _load().fa_check_args(q, k, v, mask, total_lengths, past_lengths, out, batch, heads,
+                                 kv_heads, sq, sk, kv_capacity, dim, causal, mask_planes,
+                                 local_window, scale, softcap, dtype, mask_dtype, out_layout)
+
+
+def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sk: Optional[int] = None,
+                   mask: Optional[torch.Tensor] = None,
+                   total_lengths: Optional[torch.Tensor] = None,
+                   past_lengths: Optional[torch.Tensor] = None, causal: bool = False,
+                   local_window: int = 0, scale: Optional[float] = None, softcap: float = 0.0,
+                   out_layout: str = "head", out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Attention forward on the GPU.
+
+    q [B,H,Sq,D]; k, v [B,Hkv,C,D] (C = kv capacity, ``sk`` <= C keys used, default C);
+    mask [planes,Sq,Sk] (fp32 or q's dtype); total/past lengths int32 [B] on the device.
+    Returns out [B,H,Sq,D] (``out_layout="head"``) or [B,Sq,H*D] (``"token"``).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B,H,Sq,D]; k and v [B,Hkv,C,D]")
+    B, H, Sq, D = q.shape
+    Hkv, C = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype among float32, float16, bfloat16")
+    tensors = [q, k, v, mask, total_lengths, past_lengths, out]
+    for t in tensors:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("every tensor must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("every tensor must be contiguous")
+            if t.device != q.device:
+                raise ValueError("every tensor must live on q's device")
+    sk = C if sk is None else int(sk)
+    planes = 0
+    mask_dtype = FA_DTYPE_F32
+    if mask is not None:
+        if mask.dim() != 3 or mask.shape[1] != Sq or mask.shape[2] != sk:
+            raise ValueError(f"mask must be [planes, Sq={Sq}, Sk={sk}], got {tuple(mask.shape)}")
+        if mask.dtype not in _DTYPE_CODE:
+            raise ValueError("mask must be float32 or q's dtype")
+        planes = mask.shape[0]
+        mask_dtype = _DTYPE_CODE[mask.dtype]
+    for name, t in (("total_lengths", total_lengths), ("past_lengths", past_lengths)):
+        if t is not None and (t.dtype != torch.int32 or t.shape != (B,)):
+            raise ValueError(f"{name} must be int32 [B]")
+    layout = _LAYOUT_CODE[out_layout]
+    if out is None:
+        shape = (B, H, Sq, D) if layout == 0 else (B, Sq, H * D)
+        out = torch.empty(shape, dtype=q.dtype, device=q.device)
+    elif out.dtype != q.dtype or out.numel() != B * H * Sq * D:
+        raise ValueError("out must match q's dtype and element count")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = _load()
+    status = lib.flash_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(total_lengths), _ptr(past_lengths), _ptr(out),
+        B, H, Hkv, Sq, sk, C, D, 1 if causal else 0, planes, int(local_window), float(scale),
+        float(softcap), _DTYPE_CODE[q.dtype], mask_dtype, layout, stream.cuda_stream)
+    if status != FA_OK:
+        raise FaError(status, lib.fa_last_error().decode())
+    return out

@@ -1,0 +1,192 @@
+// C ABI of libfa.so: argument validation, kernel selection and launch (declared in fa.h).
+//
+// Mirrors the host function `run` of the onnx-runtime-ep-cuda page
+// `src/kernels/flash_attention.rs` (support gate, dtype dispatch, checked narrowing of sizes,
+// grid computation, launch), with these differences: the call is asynchronous on the caller's
+// stream, sizes are validated against the stated layouts, mask planes outside {1, B, B*H} are
+// rejected instead of silently reading plane 0, and an empty key range writes zeros.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+#include "fa_params.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof(g_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Element count a*b*c*d with overflow detection; false on overflow.
+bool count4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
+    int64_t t;
+    return mul_ok(a, b, &t) && mul_ok(t, c, &t) && mul_ok(t, d, out);
+}
+
+int elem_bytes(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+
+bool aligned(const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; }
+
+struct Plan {
+    fa::FwdParams p;
+    int dp;
+    int grid;
+    int maskk;  // 0 none, 1 fp32 mask, 2 mask of the input type
+    bool empty;
+};
+
+int validate(const void* q, const void* k, const void* v, const void* mask, const void* out,
+             int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+             int mask_planes, float scale, float softcap, int dtype, int mask_dtype,
+             int out_layout, Plan* plan) {
+    g_error[0] = '\0';
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d is not one of F32 (0), F16 (1), BF16 (2)", dtype);
+    if (dim < 1 || dim > 128)
+        return fail(FA_ERR_UNSUPPORTED, "head dim %d outside the supported range 1..128", dim);
+    if (out_layout != FA_OUT_HEAD_MAJOR && out_layout != FA_OUT_TOKEN_MAJOR)
+        return fail(FA_ERR_INVALID_ARGUMENT, "out_layout %d is neither head-major (0) nor token-major (1)", out_layout);
+    if (batch < 0 || heads < 0 || sq < 0 || sk < 0 || kv_capacity < 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "negative size (batch %d, heads %d, sq %d, sk %d, kv_capacity %d)",
+                    batch, heads, sq, sk, kv_capacity);
+    if (kv_heads < 1) return fail(FA_ERR_INVALID_ARGUMENT, "kv_heads must be >= 1 (got %d)", kv_heads);
+    if (heads % kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "heads %d is not a multiple of kv_heads %d", heads, kv_heads);
+    if (sk > kv_capacity)
+        return fail(FA_ERR_INVALID_ARGUMENT, "sk %d exceeds kv_capacity %d", sk, kv_capacity);
+    const int64_t bh = (int64_t)batch * heads;
+    if (mask_planes != 0 && mask_planes != 1 && mask_planes != batch && (int64_t)mask_planes != bh)
+        return fail(FA_ERR_INVALID_ARGUMENT, "mask_planes %d is not 0, 1, batch (%d) or batch*heads (%lld)",
+                    mask_planes, batch, (long long)bh);
+    if (mask_planes < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative mask_planes %d", mask_planes);
+    if (mask_planes > 0 && mask == nullptr)
+        return fail(FA_ERR_INVALID_ARGUMENT, "mask_planes %d but the mask pointer is null", mask_planes);
+    if (mask_planes > 0 && mask_dtype != FA_DTYPE_F32 && mask_dtype != dtype)
+        return fail(FA_ERR_UNSUPPORTED, "mask dtype %d must be F32 (0) or the input dtype (%d)", mask_dtype, dtype);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (std::isnan(softcap) || std::isinf(softcap))
+        return fail(FA_ERR_INVALID_ARGUMENT, "softcap must be finite (<= 0 disables it)");
+
+    // element counts and byte sizes must fit in 63 bits
+    const int64_t esz = elem_bytes(dtype);
+    int64_t n_q, n_kv, n_mask, bytes;
+    if (!count4(batch, heads, sq, dim, &n_q) || !mul_ok(n_q, esz, &bytes))
+        return fail(FA_ERR_OVERFLOW, "q/out element count overflows");
+    if (!count4(batch, kv_heads, kv_capacity, dim, &n_kv) || !mul_ok(n_kv, esz, &bytes))
+        return fail(FA_ERR_OVERFLOW, "k/v element count overflows");
+    if (!count4(mask_planes, sq, sk, 1, &n_mask) || !mul_ok(n_mask, 4, &bytes))
+        return fail(FA_ERR_OVERFLOW, "mask element count overflows");
+
+    plan->empty = (n_q == 0);
+    if (plan->empty) return FA_OK;
+    if (q == nullptr || out == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "q and out must not be null");
+    if (sk > 0 && (k == nullptr || v == nullptr))
+        return fail(FA_ERR_INVALID_ARGUMENT, "k and v must not be null when sk > 0");
+
+    const int64_t q_tiles = ((int64_t)sq + fa::kBlockRows - 1) / fa::kBlockRows;
+    const int64_t pairs = (int64_t)batch * q_tiles;
+    const int64_t pairs_padded = (pairs + 7) / 8 * 8;
+    int64_t grid;
+    if (!mul_ok(pairs_padded, heads, &grid) || grid > 0x7fffffffLL)
+        return fail(FA_ERR_OVERFLOW, "grid of %lld x %d workgroups exceeds the launch limit",
+                    (long long)pairs_padded, heads);
+
+    fa::FwdParams& p = plan->p;
+    p.q = q; p.k = k; p.v = v; p.out = (void*)out;
+    p.mask = mask_planes > 0 ? mask : nullptr;
+    p.batch = batch; p.heads = heads; p.kv_heads = kv_heads; p.sq = sq; p.sk = sk; p.dim = dim;
+    p.group = heads / kv_heads;
+    p.mask_planes = mask_planes;
+    p.q_tiles = (int)q_tiles;
+    p.pairs = (int)pairs;
+    p.kv_capacity = kv_capacity;
+    const uintptr_t vec_align = 16;
+    p.vec_kv = (dim % (dtype == FA_DTYPE_F32 ? 4 : 8) == 0) && aligned(q, vec_align) &&
+               (sk == 0 || (aligned(k, vec_align) && aligned(v, vec_align)));
+    p.vec_out = (dim % 4 == 0) && aligned(out, dtype == FA_DTYPE_F32 ? 16 : 8);
+    plan->maskk = mask_planes == 0 ? 0 : (mask_dtype == FA_DTYPE_F32 ? 1 : 2);
+    p.vec_mask = mask_planes > 0 && sk % 4 == 0 && aligned(mask, plan->maskk == 1 ? 16 : 8);
+    if (out_layout == FA_OUT_HEAD_MAJOR) {
+        p.o_stride_b = (int64_t)heads * sq * dim;
+        p.o_stride_h = (int64_t)sq * dim;
+        p.o_stride_i = dim;
+    } else {
+        p.o_stride_b = (int64_t)sq * heads * dim;
+        p.o_stride_h = dim;
+        p.o_stride_i = (int64_t)heads * dim;
+    }
+    p.scale = scale;
+    p.softcap = softcap > 0.0f ? softcap : 0.0f;
+    const bool has_cap = softcap > 0.0f;
+    p.cap_y = has_cap ? scale / softcap : 0.0f;
+    // Units of the tracked score x and the log2(e) factor that turns them into base-2 exponents.
+    const float raw_k = scale * 1.4426950408889634f;
+    p.raw_scores = (!has_cap && mask_planes == 0 && scale > 0.0f && std::isnormal(raw_k) && raw_k >= 1e-30f) ? 1 : 0;
+    if (has_cap && mask_planes == 0) p.kfac = softcap * 1.4426950408889634f;  // x = tanh(.)
+    else if (p.raw_scores) p.kfac = raw_k;                                    // x = raw dot
+    else p.kfac = 1.4426950408889634f;                                        // x in natural units
+    if (!std::isfinite(p.kfac) || !(p.kfac > 0.0f))
+        return fail(FA_ERR_UNSUPPORTED, "softcap %g is too large for fp32 exponent scaling", (double)softcap);
+    plan->dp = (dim + 31) / 32 * 32;
+    plan->grid = (int)grid;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_check_args(const void* q, const void* k, const void* v, const void* mask,
+                  const int32_t* total_lengths, const int32_t* past_lengths, const void* out,
+                  int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                  int causal, int mask_planes, int local_window, float scale, float softcap,
+                  int dtype, int mask_dtype, int out_layout) {
+    (void)total_lengths; (void)past_lengths; (void)causal; (void)local_window;
+    Plan plan;
+    return validate(q, k, v, mask, out, batch, heads, kv_heads, sq, sk, kv_capacity, dim,
+                    mask_planes, scale, softcap, dtype, mask_dtype, out_layout, &plan);
+}
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
+                   const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                   int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                   int causal, int mask_planes, int local_window, float scale, float softcap,
+                   int dtype, int mask_dtype, int out_layout, void* stream) {
+    Plan plan;
+    const int st = validate(q, k, v, mask, out, batch, heads, kv_heads, sq, sk, kv_capacity, dim,
+                            mask_planes, scale, softcap, dtype, mask_dtype, out_layout, &plan);
+    if (st != FA_OK || plan.empty) return st;
+    fa::FwdParams& p = plan.p;
+    p.total_lengths = total_lengths;
+    p.past_lengths = past_lengths;
+    p.causal = causal != 0;
+    p.window = local_window > 0 ? local_window : 0;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();  // a stale error from unrelated work must not be reported as ours
+    hipError_t err;
+    if (dtype == FA_DTYPE_BF16) err = fa::launch_bf16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
+    else if (dtype == FA_DTYPE_F16) err = fa::launch_f16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
+    else err = fa::launch_f32(p, plan.dp, plan.grid, plan.maskk != 0, p.softcap > 0.0f, s);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return FA_OK;
+}
+
+const char* fa_last_error(void) { return g_error; }
+
+const char* fa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

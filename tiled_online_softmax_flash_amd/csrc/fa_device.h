@@ -1,0 +1,116 @@
+// Device helpers shared by the attention kernels: work decoding, the per-row key rule,
+// tile classification and a few arithmetic primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// 2^x on the hardware exponential unit (v_exp_f32); -inf -> 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh(y).  For |y| >= 1/8 it uses the identity tanh y = 1 - 2 / (e^{2y} + 1) on the hardware
+// exponential and reciprocal (absolute error a few fp32 ulps of 1, relative error below 1e-6
+// there); it saturates cleanly to +-1.  For |y| < 1/8 the identity would cancel, so the odd
+// Taylor series y - y^3/3 + 2y^5/15 - 17y^7/315 is used instead (truncation below 2e-9
+// relative).  Relative accuracy near 0 matters when a huge softcap multiplies the result.
+__device__ __forceinline__ float tanh_fast(float y) {
+    const float e = exp2_hw(y * (2.0f * kLog2e));
+    const float big = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+    const float y2 = y * y;
+    const float poly = __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, -17.0f / 315.0f, 2.0f / 15.0f), -1.0f / 3.0f), 1.0f);
+    const float small = y * poly;
+    return __builtin_fabsf(y) < 0.125f ? small : big;
+}
+
+// One workgroup's share of the problem: batch b, query head h, query tile qt.
+struct WorkItem {
+    int b, h, qt;
+    bool valid;
+};
+
+// Workgroups are dealt to the 8 XCDs round-robin by block id.  The decode keeps all query heads
+// of one (batch, query tile) pair on one XCD, so that heads sharing K/V (a GQA group) or a mask
+// plane read them through the same L2, and deals pairs to XCDs round-robin in descending order
+// of query tile (causal tiles late in the sequence carry the most keys, so they start first).
+// The grid holds ceil(pairs / 8) * 8 * heads blocks; blocks of the padding pairs exit at once.
+__device__ __forceinline__ WorkItem decode_work(const FwdParams& p, int bid) {
+    WorkItem w;
+    const int xcd = bid & 7;
+    const int slot = bid >> 3;
+    const int pair_local = slot / p.heads;
+    w.h = slot - pair_local * p.heads;
+    const int pair = pair_local * 8 + xcd;
+    w.valid = pair < p.pairs;
+    w.qt = p.q_tiles - 1 - pair / p.batch;
+    w.b = pair - (pair / p.batch) * p.batch;
+    return w;
+}
+
+// The key rule of one batch entry (see fa.h): key j is attended by query row i iff
+// lo(i) <= j <= hi(i).  Both bounds are non-decreasing in i.
+struct KeyRule {
+    int64_t L;      // min(total, sk), at least 0
+    int64_t base;   // cmax(i) = base + i
+    int64_t window;
+    int causal;
+
+    __device__ __forceinline__ int64_t lo(int64_t i) const {
+        if (window <= 0) return 0;
+        const int64_t v = base + i + 1 - window;
+        return v > 0 ? v : 0;
+    }
+    __device__ __forceinline__ int64_t hi(int64_t i) const {
+        const int64_t cm = base + i;
+        return (causal && cm < L - 1) ? cm : L - 1;
+    }
+};
+
+__device__ __forceinline__ KeyRule make_rule(const FwdParams& p, int b) {
+    KeyRule r;
+    int64_t L = p.sk;
+    if (p.total_lengths != nullptr) {
+        const int64_t t = p.total_lengths[b];
+        if (t < L) L = t;
+    }
+    if (L < 0) L = 0;
+    r.L = L;
+    r.base = p.past_lengths != nullptr ? (int64_t)p.past_lengths[b] : L - p.sq;
+    r.window = p.window;
+    r.causal = p.causal;
+    return r;
+}
+
+// Mask plane of (b, h): 0, b, or b*heads + h (tested in that order).
+__device__ __forceinline__ int64_t mask_plane(const FwdParams& p, int b, int h) {
+    if (p.mask_planes == p.batch) return b;
+    if (p.mask_planes == p.batch * p.heads) return (int64_t)b * p.heads + h;
+    return 0;
+}
+
+// Row of the key tile held in LDS row r (0..31) of a 32-key block.  A 32x32 MFMA accumulator
+// gives lane (m, half) the values of rows 8*(v/4) + 4*half + v%4; storing key kk(r) in row r
+// makes those rows hold keys 16*half + v, i.e. each lane owns 16 consecutive keys.
+__device__ __forceinline__ int lds_row_of_key(int key_in_block) {
+    const int half = key_in_block >> 4;
+    const int v = key_in_block & 15;
+    return 8 * (v >> 2) + 4 * half + (v & 3);
+}
+
+// Wave-level any() of a per-lane predicate.
+__device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
+
+}  // namespace fa

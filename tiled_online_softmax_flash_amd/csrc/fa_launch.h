@@ -1,0 +1,13 @@
+// Per-dtype launch entry points, one translation unit each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_params.h"
+
+namespace fa {
+// maskk: 0 none, 1 fp32 mask, 2 mask of the input type.  dp: head dim padded to 32/64/96/128.
+hipError_t launch_bf16(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
+hipError_t launch_f16(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
+hipError_t launch_f32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s);
+}  // namespace fa

@@ -1,0 +1,41 @@
+// Launch parameters shared by the host dispatcher and the attention kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Rows per workgroup for every kernel: four 64-lane waves of 32 query rows each.
+constexpr int kBlockRows = 128;
+constexpr int kWaveRows = 32;
+constexpr int kThreads = 256;
+
+// Lazy rescaling threshold, in log2 units: the running row maximum is only moved when a
+// new score exceeds it by more than this, so unnormalised probabilities stay <= 2^8.
+constexpr float kRescaleLog2 = 8.0f;
+
+struct FwdParams {
+    const void* q;               // [batch, heads, sq, dim]
+    const void* k;               // [batch, kv_heads, kv_capacity, dim]
+    const void* v;               // [batch, kv_heads, kv_capacity, dim]
+    const void* mask;            // [mask_planes, sq, sk] or null
+    const int32_t* total_lengths;
+    const int32_t* past_lengths;
+    void* out;
+    int batch, heads, kv_heads, sq, sk, dim, group;
+    int causal, window, mask_planes;
+    int q_tiles;                 // ceil(sq / kBlockRows)
+    int pairs;                   // batch * q_tiles: (batch, query tile) pairs
+    int vec_kv;                  // q/k/v rows move in 16-byte pieces (dim and pointers allow it)
+    int vec_mask;                // mask rows move in 16-byte pieces
+    int vec_out;                 // output rows move in 4-element pieces
+    int raw_scores;              // 1: scores stay raw dot products, scale folded into kfac
+    float scale;
+    float softcap;
+    float cap_y;                 // scale / softcap: dot product -> tanh argument
+    float kfac;                  // log2(e) per unit of the tracked score
+    int64_t kv_capacity;
+    int64_t o_stride_b, o_stride_h, o_stride_i;  // output strides in elements
+};
+
+}  // namespace fa

@@ -97,8 +97,15 @@ class Problem:
         return Problem(**moved)
 
 
-def _normal(rng: np.random.Generator, shape, dtype: str, amp: float = 1.0) -> torch.Tensor:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
+def _normal(rng: np.random.Generator, shape, dtype: str, amp: float = 1.0,
+            dist: str = "normal") -> torch.Tensor:
+    if dist == "normal":
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+    elif dist == "neg_uniform":
+        # one-signed values in [-1, 0), the range of the prior-art parity test's generator
+        x = -rng.random(size=shape, dtype=np.float32)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
     if amp != 1.0:
         x = x * np.float32(amp)
     return torch.from_numpy(x).to(_TORCH_DTYPES[dtype])
@@ -121,6 +128,7 @@ def make_problem(
     scale: Optional[float] = None,
     softcap: float = 0.0,
     amp: float = 1.0,
+    dist: str = "normal",
     lengths: Optional[str] = None,
     max_past: int = 0,
     nan_beyond_total: bool = False,
@@ -138,12 +146,13 @@ def make_problem(
     ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0) or ``"normal"``
     (finite N(0,1) values with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
     ``dead_rows``: query rows per mask plane set entirely to -inf.
+    ``dist``: ``"normal"`` (N(0,1)) or ``"neg_uniform"`` (U[-1,0)), times ``amp``.
     """
     capacity = sk if kv_capacity is None else kv_capacity
     rng = np.random.Generator(np.random.PCG64(seed))
-    q = _normal(rng, (batch, heads, sq, dim), dtype, amp)
-    k = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp)
-    v = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp)
+    q = _normal(rng, (batch, heads, sq, dim), dtype, amp, dist)
+    k = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
+    v = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
 
     total = past = None
     if lengths == "past":
@@ -226,7 +235,7 @@ WORKLOADS = {
 # the full oracle to finish in seconds while still spanning several tiles and a ragged tail.
 SMALL_WORKLOADS = {
     "tiny": dict(WORKLOADS["tiny"]),
-    "dit_joint": dict(WORKLOADS["dit_joint"], heads=3, sq=333, sk=333),
+    "dit_joint": dict(WORKLOADS["dit_joint"], heads=3, kv_heads=3, sq=333, sk=333),
     "gqa_causal": dict(WORKLOADS["gqa_causal"], batch=2, heads=8, kv_heads=2, sq=300, sk=300),
     "kv_cache_prefill": dict(
         WORKLOADS["kv_cache_prefill"], batch=3, heads=8, kv_heads=2, sq=77, sk=640, kv_capacity=640,
