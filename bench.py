@@ -110,6 +110,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="gqa_causal", choices=list(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of attention, run --steps plain device copies of BYTES bytes "
+                         "(reference for scaling FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -119,6 +122,17 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                          "launches": args.steps}), flush=True)
+        return 0
 
     prob = workloads.workload(args.workload)
     work = problem_work(prob)

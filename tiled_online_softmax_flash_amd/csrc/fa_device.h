@@ -110,6 +110,33 @@ __device__ __forceinline__ int lds_row_of_key(int key_in_block) {
     return 8 * (v >> 2) + 4 * half + (v & 3);
 }
 
+// Raw buffer descriptor (gfx9 family: stride 0, byte-addressed, dword 3 = 0x00020000) over
+// `bytes` bytes at `base`.  Buffer loads at offsets past `bytes` return 0 without touching
+// memory, which is how tiles ending past the last valid key are zero-filled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// max(x[lane % 32], x[32 + lane % 32]) in every lane: the row maximum of the two lanes that
+// share a query row, via v_permlane32_swap (a VALU op, no LDS crossbar).
+__device__ __forceinline__ float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// x[lane % 32] + x[32 + lane % 32] in every lane.
+__device__ __forceinline__ float half_swap_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+constexpr int kSchedVmemRead = 0x020;
+
 // Wave-level any() of a per-lane predicate.
 __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
 

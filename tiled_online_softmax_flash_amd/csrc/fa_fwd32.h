@@ -11,7 +11,8 @@
 
 namespace fa {
 
-template <int DP, bool MASKED, bool SOFTCAP>
+// RAW: no mask, no softcap and scale > 0 (scale folded into the base-2 exponent factor).
+template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 fwd32_kernel(const FwdParams p) {
     constexpr int BN = 32;
@@ -34,7 +35,7 @@ fwd32_kernel(const FwdParams p) {
     const int b = w.b, h = w.h;
     const int kvh = h / p.group;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
     const int lane = tid & 63;
     const int lr = lane & 31;
     const int hh = lane >> 5;
@@ -50,6 +51,10 @@ fwd32_kernel(const FwdParams p) {
     const bool row_valid = row < p.sq;
     const int64_t my_lo = row_valid ? rule.lo(row) : 1;
     const int64_t my_hi = row_valid ? rule.hi(row) : 0;
+    // 32-bit copies for the per-element test on partial tiles: keys are < sk <= INT32_MAX, so a
+    // lower bound above INT32_MAX or an upper bound below -1 leaves the row just as empty.
+    const int my_lo32 = (int)(my_lo < 0x7fffffffLL ? my_lo : 0x7fffffffLL);
+    const int my_hi32 = (int)(my_hi > -1 ? my_hi : -1);
     const int64_t w_lo_min = rule.lo(wr0), w_lo_max = rule.lo(wr1);
     const int64_t w_hi_min = rule.hi(wr0), w_hi_max = rule.hi(wr1);
 
@@ -202,24 +207,35 @@ fwd32_kernel(const FwdParams p) {
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s, 0, 0, 0);
         }
 
+        auto epi = [&](float sv, float mv) -> float {
+            if constexpr (SOFTCAP) {
+                const float th = tanh_fast(sv * p.cap_y);
+                return MASKED ? __builtin_fmaf(p.softcap, th, mv) : th;
+            } else if constexpr (MASKED) {
+                return __builtin_fmaf(sv, p.scale, mv);
+            } else {
+                return RAW ? sv : sv * p.scale;
+            }
+        };
         float mt = neg_inf();
+        if (full) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float x = s[v];
-            if (SOFTCAP) {
-                const float th = tanh_fast(x * p.cap_y);
-                x = MASKED ? __builtin_fmaf(p.softcap, th, mval[v]) : th;
-            } else if (MASKED) {
-                x = __builtin_fmaf(x, p.scale, mval[v]);
-            } else if (!p.raw_scores) {
-                x = x * p.scale;
+            for (int v = 0; v < 16; ++v) {
+                const float x = epi(s[v], MASKED ? mval[v] : 0.0f);
+                s[v] = x;
+                mt = __builtin_fmaxf(mt, x);
             }
-            if (!full) {
-                const int64_t j = k0 + 16 * hh + v;
-                x = (j >= my_lo && j <= my_hi) ? x : neg_inf();
+        } else {
+            const int base = (int)k0 + 16 * hh;
+            const int lo_rel = my_lo32 - base;
+            const int hi_rel = my_hi32 - base;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float x = epi(s[v], MASKED ? mval[v] : 0.0f);
+                x = (v >= lo_rel && v <= hi_rel) ? x : neg_inf();
+                s[v] = x;
+                mt = __builtin_fmaxf(mt, x);
             }
-            s[v] = x;
-            mt = __builtin_fmaxf(mt, x);
         }
         mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
 
@@ -302,16 +318,19 @@ fwd32_kernel(const FwdParams p) {
     }
 }
 
-template <int DP, bool MASKED, bool SOFTCAP>
+template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
 hipError_t launch_fwd32_one(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd32_kernel<DP, MASKED, SOFTCAP>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd32_kernel<DP, MASKED, SOFTCAP, RAW>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DP>
 hipError_t launch_fwd32_dp(const FwdParams& p, int grid, bool masked, bool softcap, hipStream_t s) {
-    if (softcap) return masked ? launch_fwd32_one<DP, true, true>(p, grid, s) : launch_fwd32_one<DP, false, true>(p, grid, s);
-    return masked ? launch_fwd32_one<DP, true, false>(p, grid, s) : launch_fwd32_one<DP, false, false>(p, grid, s);
+    if (softcap) return masked ? launch_fwd32_one<DP, true, true, false>(p, grid, s)
+                               : launch_fwd32_one<DP, false, true, false>(p, grid, s);
+    if (masked) return launch_fwd32_one<DP, true, false, false>(p, grid, s);
+    return p.raw_scores ? launch_fwd32_one<DP, false, false, true>(p, grid, s)
+                        : launch_fwd32_one<DP, false, false, false>(p, grid, s);
 }
 
 inline hipError_t launch_fwd32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s) {
