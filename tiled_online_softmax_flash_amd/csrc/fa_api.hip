@@ -15,6 +15,7 @@
 #include "../../include/fa.h"
 #include "fa_launch.h"
 #include "fa_params.h"
+#include "fa_fwd16_ring_consts.h"
 
 namespace {
 
@@ -45,6 +46,7 @@ struct Plan {
     int dp;
     int grid;
     int maskk;  // 0 none, 1 fp32 mask, 2 mask of the input type
+    bool ring;  // 256-row LDS-ring kernel (16-bit, head dim 64/128, aligned rows)
     bool empty;
 };
 
@@ -96,7 +98,15 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     if (sk > 0 && (k == nullptr || v == nullptr))
         return fail(FA_ERR_INVALID_ARGUMENT, "k and v must not be null when sk > 0");
 
-    const int64_t q_tiles = ((int64_t)sq + fa::kBlockRows - 1) / fa::kBlockRows;
+    // kernel choice: the LDS-ring kernel takes 16-bit inputs with head dim 64 or 128 whose rows
+    // (and the output rows) sit on 16-byte boundaries
+    plan->ring = dtype != FA_DTYPE_F32 && (dim == 64 || dim == 128) && aligned(q, 16) &&
+                 aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16)));
+    const int block_rows = plan->ring ? fa::kRingBlockRows : fa::kBlockRows;
+    if (mask_planes > 0 && (int64_t)block_rows * sk * 4 >= 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "sk %d is too long for a masked launch (a workgroup's mask rows "
+                    "must span less than 2 GiB)", sk);
+    const int64_t q_tiles = ((int64_t)sq + block_rows - 1) / block_rows;
     const int64_t pairs = (int64_t)batch * q_tiles;
     const int64_t pairs_padded = (pairs + 7) / 8 * 8;
     int64_t grid;
@@ -178,8 +188,12 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();  // a stale error from unrelated work must not be reported as ours
     hipError_t err;
-    if (dtype == FA_DTYPE_BF16) err = fa::launch_bf16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
-    else if (dtype == FA_DTYPE_F16) err = fa::launch_f16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
+    if (dtype == FA_DTYPE_BF16)
+        err = plan.ring ? fa::launch_bf16_ring(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s)
+                        : fa::launch_bf16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
+    else if (dtype == FA_DTYPE_F16)
+        err = plan.ring ? fa::launch_f16_ring(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s)
+                        : fa::launch_f16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
     else err = fa::launch_f32(p, plan.dp, plan.grid, plan.maskk != 0, p.softcap > 0.0f, s);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;

@@ -137,6 +137,52 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int kSchedDsWrite = 0x200;
 constexpr int kSchedVmemRead = 0x020;
 
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16-byte buffer load straight into LDS: lane l's 16 bytes (from `voffset` within the buffer
+// described by `rsrc`) land at LDS byte address `lds_addr + 16 * l`.  Issued through inline asm
+// so that the compiler's wait-count pass leaves these loads to the kernel's own waits
+// (dma_wait) instead of draining all vector-memory loads before every LDS read.
+__device__ __forceinline__ void dma_lds16(u32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "m0");
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight (loads retire in order).
+template <int N>
+__device__ __forceinline__ void dma_wait() {
+    static_assert(N >= 0 && N <= 15, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else static_assert(N == 0, "add the vmcnt value");
+}
+
+// Raw buffer descriptor as four wave-uniform dwords (gfx9 family, stride 0, byte-addressed).
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, int bytes) {
+    const uint64_t a = (uint64_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
 // Wave-level any() of a per-lane predicate.
 __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
 
