@@ -100,8 +100,12 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
 
     // kernel choice: the LDS-ring kernel takes 16-bit inputs with head dim 64 or 128 whose rows
     // (and the output rows) sit on 16-byte boundaries
+    // (a mask must have 16-byte aligned rows there: sk a multiple of 4 and an aligned base)
+    const int maskk = mask_planes == 0 ? 0 : (mask_dtype == FA_DTYPE_F32 ? 1 : 2);
+    const bool mask_vec = mask_planes > 0 && sk % 4 == 0 && aligned(mask, maskk == 1 ? 16 : 8);
     plan->ring = dtype != FA_DTYPE_F32 && (dim == 64 || dim == 128) && aligned(q, 16) &&
-                 aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16)));
+                 aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16))) &&
+                 (mask_planes == 0 || mask_vec);
     const int block_rows = plan->ring ? fa::kRingBlockRows : fa::kBlockRows;
     if (mask_planes > 0 && (int64_t)block_rows * sk * 4 >= 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "sk %d is too long for a masked launch (a workgroup's mask rows "
@@ -109,8 +113,11 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     const int64_t q_tiles = ((int64_t)sq + block_rows - 1) / block_rows;
     const int64_t pairs = (int64_t)batch * q_tiles;
     const int64_t pairs_padded = (pairs + 7) / 8 * 8;
+    // group-major workgroup order when no mask plane is shared across heads and the (batch, KV
+    // head) groups split evenly over the 8 XCDs; the grid then needs no padding
+    const bool xcd_groups = mask_planes == 0 && ((int64_t)batch * kv_heads) % 8 == 0;
     int64_t grid;
-    if (!mul_ok(pairs_padded, heads, &grid) || grid > 0x7fffffffLL)
+    if (!mul_ok(xcd_groups ? (int64_t)batch * q_tiles : pairs_padded, heads, &grid) || grid > 0x7fffffffLL)
         return fail(FA_ERR_OVERFLOW, "grid of %lld x %d workgroups exceeds the launch limit",
                     (long long)pairs_padded, heads);
 
@@ -122,13 +129,14 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     p.mask_planes = mask_planes;
     p.q_tiles = (int)q_tiles;
     p.pairs = (int)pairs;
+    p.xcd_groups = xcd_groups ? 1 : 0;
     p.kv_capacity = kv_capacity;
     const uintptr_t vec_align = 16;
     p.vec_kv = (dim % (dtype == FA_DTYPE_F32 ? 4 : 8) == 0) && aligned(q, vec_align) &&
                (sk == 0 || (aligned(k, vec_align) && aligned(v, vec_align)));
     p.vec_out = (dim % 4 == 0) && aligned(out, dtype == FA_DTYPE_F32 ? 16 : 8);
-    plan->maskk = mask_planes == 0 ? 0 : (mask_dtype == FA_DTYPE_F32 ? 1 : 2);
-    p.vec_mask = mask_planes > 0 && sk % 4 == 0 && aligned(mask, plan->maskk == 1 ? 16 : 8);
+    plan->maskk = maskk;
+    p.vec_mask = mask_vec;
     if (out_layout == FA_OUT_HEAD_MAJOR) {
         p.o_stride_b = (int64_t)heads * sq * dim;
         p.o_stride_h = (int64_t)sq * dim;

@@ -42,15 +42,34 @@ struct WorkItem {
     bool valid;
 };
 
-// Workgroups are dealt to the 8 XCDs round-robin by block id.  The decode keeps all query heads
-// of one (batch, query tile) pair on one XCD, so that heads sharing K/V (a GQA group) or a mask
-// plane read them through the same L2, and deals pairs to XCDs round-robin in descending order
-// of query tile (causal tiles late in the sequence carry the most keys, so they start first).
-// The grid holds ceil(pairs / 8) * 8 * heads blocks; blocks of the padding pairs exit at once.
+// Workgroups are dealt to the 8 XCDs round-robin by block id; each XCD has its own L2.  Two
+// orders are used:
+//   * group-major (p.xcd_groups != 0, requires batch * kv_heads to be a multiple of 8): every
+//     workgroup of one (batch, KV head) group -- all its query heads and query tiles -- runs on
+//     one XCD, so the group's K/V rows are fetched into that L2 once and then shared.  Groups
+//     are dealt to XCDs round-robin; inside a group, query tiles go in descending order (causal
+//     tiles late in the sequence carry the most keys, so they start first).
+//   * pair-major: all query heads of one (batch, query tile) pair run on one XCD, so heads that
+//     share a mask plane read it through the same L2; pairs are dealt round-robin in descending
+//     query-tile order.  The grid holds ceil(pairs / 8) * 8 * heads blocks; blocks of the
+//     padding pairs exit at once.
 __device__ __forceinline__ WorkItem decode_work(const FwdParams& p, int bid) {
     WorkItem w;
     const int xcd = bid & 7;
     const int slot = bid >> 3;
+    if (p.xcd_groups) {
+        const int per_group = p.group * p.q_tiles;
+        const int gl = slot / per_group;
+        const int r = slot - gl * per_group;
+        const int grp = gl * 8 + xcd;                 // b * kv_heads + kvh
+        const int qr = r / p.group;
+        const int hg = r - qr * p.group;
+        w.b = grp / p.kv_heads;
+        w.h = (grp - w.b * p.kv_heads) * p.group + hg;
+        w.qt = p.q_tiles - 1 - qr;
+        w.valid = w.b < p.batch;
+        return w;
+    }
     const int pair_local = slot / p.heads;
     w.h = slot - pair_local * p.heads;
     const int pair = pair_local * 8 + xcd;

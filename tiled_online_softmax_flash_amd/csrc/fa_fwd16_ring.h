@@ -5,20 +5,27 @@
 // `flash_attention_body`), laid out for a whole CDNA4 compute unit per workgroup:
 //
 //   * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU, 2 waves per SIMD.
-//     Every K/V tile staged in LDS now serves 256 rows (half the L2->LDS traffic per flop of a
-//     128-row tile).
+//     Every K/V tile staged in LDS serves 256 rows.
 //   * K/V tiles of 64 keys stream through a 4-slot LDS ring with 16-byte buffer-to-LDS loads
 //     (no staging registers), issued three tiles ahead; one barrier per tile.  Each tile's
 //     buffer descriptor ends at the last valid key, so rows past the cache length arrive as 0.
-//   * LDS layouts are chosen lane by lane through the DMA source addresses:
-//       K: row r of a 32-row half holds key kk(r) (see lds_row_of_key) and its 16-byte chunk c
-//          sits at position c ^ k_swz(r), so the 16 rows one 16-byte read cycle touches hit 16
-//          different bank slots;
-//       V: row-major V[key][d], chunk c of key j at c ^ v_swz(j).  V^T operands come from
-//          ds_read_b64_tr_b16, which transposes 4 keys x 4 dims per 16-lane group, so V is never
-//          transposed in registers.
-//   * Compute per half-tile of 32 keys as in fa_fwd16.h: S^T = K Q^T on 32x32x16 MFMA,
-//     softmax on the VALU overlapped with the next half-tile's MFMAs, then O^T += V^T P^T.
+//     K slots fill the lower part of the LDS and V slots the upper part, and the tile loop is
+//     unrolled by the ring depth, so every LDS operand read is a per-lane base register plus
+//     an immediate offset.
+//   * LDS layouts are chosen lane by lane through the DMA source addresses.  Each 32-key half of
+//     a tile is stored operand-block-major, so that one per-lane base address serves every MFMA
+//     operand of a block and the bank pattern holds without per-read swizzle arithmetic:
+//       K: [16-dim slice ks][row r][32 bytes]; row r holds key kk(r) (see lds_row_of_key) and
+//          its two 16-byte chunks trade places when bit 3 of r is set, so the 16 rows one
+//          16-byte read cycle touches hit 16 different bank slots;
+//       V: [32-dim block db][key][64 bytes].  V^T operands come from ds_read_b64_tr_b16, which
+//          transposes 4 keys x 4 dims per 16-lane group; the 4 consecutive keys one read cycle
+//          touches fill all 64 banks.  V is never transposed in registers.
+//   * Work per half-tile of 32 keys: S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA.  The
+//     schedule is software-pipelined by one half-tile: block u issues the P.V products of
+//     half-tile u-1 and the Q.K products of half-tile u+1 back to back on the matrix cores and
+//     spreads the softmax of half-tile u (VALU) between them, so that both units stay busy in
+//     every wave.
 #pragma once
 
 #include <type_traits>
@@ -29,6 +36,36 @@
 
 namespace fa {
 
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
+// Mask values of one half-tile for one lane (16 keys), exactly as loaded: fp32 words, or
+// 16-bit values packed two per word.
+template <int MASKK> struct MaskHalf {};
+template <> struct MaskHalf<kMaskF32> { u32x4 w[4]; };
+template <> struct MaskHalf<kMaskT> { u32x2 w[4]; };
+
+// Vector loads issued through inline asm, like the K/V ring's DMA: the kernel places their
+// waits itself (they retire before the dma_wait that ends the ring step after their issue),
+// where the compiler's wait-count pass would drain the whole K/V ring in flight.  Their result
+// registers must not be read before that wait; launder() hands them on after it.
+__device__ __forceinline__ u32x4 vload_b128(u32x4 rsrc, uint32_t voff) {
+    u32x4 r;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc));
+    return r;
+}
+__device__ __forceinline__ u32x2 vload_b64(u32x4 rsrc, uint32_t voff) {
+    u32x2 r;
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc));
+    return r;
+}
+template <int MASKK>
+__device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
+    if constexpr (MASKK != kMaskNone) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(m.w[c]));
+    }
+}
 
 template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
@@ -44,16 +81,20 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int ROWB = DP * 2;                 // bytes per K/V row
     constexpr int CPR = DP / 8;                  // 16-byte chunks per row
     constexpr int TILE_BYTES = BN * ROWB;
-    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
+    constexpr int V_REGION = STAGES * TILE_BYTES;   // K slots [0, V_REGION), V slots after
     constexpr int LDW = TILE_BYTES / 1024 / WAVES;  // 1 KiB DMA ops per wave per operand per tile
-    constexpr int NKS = DP / 16;
-    constexpr int NDB = DP / 32;
+    constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
+    constexpr int NDB = DP / 32;                 // 32-dim output blocks
+    constexpr int NMF = 2 * NDB + NKS;           // MFMAs per pipelined block
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
+    using MaskH = MaskHalf<MASKK>;
     static_assert(DP == 64 || DP == 128, "ring kernel covers head dims 64 and 128");
     static_assert(LDW >= 1, "tile must cover every wave");
+    static_assert((STAGES - 1) * TILE_BYTES + HB * ROWB + 12 * ROWB + 8 < 65536,
+                  "LDS operand offsets must fit the 16-bit immediate");
 
-    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGES * TILE_BYTES];
     const uint32_t lds_base = lds_addr(lds);
 
     const WorkItem w = decode_work(p, blockIdx.x);
@@ -109,14 +150,14 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     }
 
-    // ---- mask rows of this workgroup
+    // ---- mask rows of this workgroup (rows are 16-byte aligned: the dispatcher checks it)
     constexpr uint32_t MESZ = MASKK == kMaskF32 ? 4u : 2u;
-    __amdgpu_buffer_rsrc_t rmask;
+    u32x4 rmask = u32x4{0u, 0u, 0u, 0u};
     uint32_t mask_row_off = 0;
     if constexpr (MASKED) {
         const int64_t rows_here = q_last - q0 + 1;
         const char* mbase = (const char*)p.mask + ((mask_plane(p, b, h) * p.sq + q0) * (int64_t)p.sk) * MESZ;
-        rmask = make_rsrc(mbase, (int)(rows_here * p.sk * MESZ));
+        rmask = make_rsrc_words(mbase, (int)(rows_here * p.sk * MESZ));
         mask_row_off = (uint32_t)((row - q0) * (int64_t)p.sk) * MESZ;
     }
 
@@ -128,24 +169,28 @@ fwd16_ring_kernel(const FwdParams p) {
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
-    // ---- LDS swizzles (the LDS serves 256 bytes per cycle: 16 lanes of a 16-byte read, 32 lanes
-    // of an 8-byte read).  K: the 16 rows one read cycle touches sit in 16 distinct 16-byte bank
-    // slots.  V: the 4 keys x 2 halves of dims one transpose-read cycle touches likewise.
-    auto k_swz = [](int r) -> int { return DP == 128 ? (r & 15) : ((r >> 1) & 7); };
-    auto v_swz = [](int key) -> int { return DP == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); };
-
-    // ---- DMA source offsets: DMA op i of a tile writes physical chunks [64 i, 64 i + 64)
+    // ---- DMA source offsets: DMA op i of a tile writes physical 16-byte chunks [64 i, 64 i + 64)
+    // (K and V alike); a half-tile holds HB * CPR chunks.  With q the chunk index inside half H:
+    //   K chunk pc of half H: slice ks = q / 64, row r = (q / 2) % 32, position c = q % 2
+    //     (q = pc within the half) <- key 32 H + kk(r), dim chunk 2 ks + (c ^ bit 3 of r);
+    //   V chunk pc of half H: block db = q / 128, key j = (q / 4) % 32, chunk c = q % 4
+    //     <- key 32 H + j, dim chunk 4 db + c.
+    constexpr int HALF_CHUNKS = HB * CPR;
     uint32_t k_src[LDW], v_src[LDW];
 #pragma unroll
     for (int j = 0; j < LDW; ++j) {
         const int pc = 64 * (wave * LDW + j) + lane;   // physical chunk index in the tile
-        const int prow = pc / CPR;
-        const int pch = pc % CPR;
-        const int kkey = (prow & ~31) + [](int r) {   // key held by LDS row r (inverse of lds_row_of_key)
-            return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-        }(prow & 31);
-        k_src[j] = (uint32_t)(kkey * ROWB + ((pch ^ k_swz(prow)) * 16));
-        v_src[j] = (uint32_t)(prow * ROWB + ((pch ^ v_swz(prow)) * 16));
+        const int hf = pc / HALF_CHUNKS;
+        const int q = pc % HALF_CHUNKS;
+        {
+            const int ks = q / 64, r = (q >> 1) & 31, c = q & 1;
+            const int key = 32 * hf + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);   // kk(r)
+            k_src[j] = (uint32_t)(key * ROWB + (2 * ks + (c ^ ((r >> 3) & 1))) * 16);
+        }
+        {
+            const int db = q / 128, key = 32 * hf + ((q >> 2) & 31), c = q & 3;
+            v_src[j] = (uint32_t)(key * ROWB + (4 * db + c) * 16);
+        }
     }
 
     auto issue_tile = [&](int t) __attribute__((always_inline)) {
@@ -158,8 +203,9 @@ fwd16_ring_kernel(const FwdParams p) {
         const int64_t base_off = keys > 0 ? k0 * ROWB : 0;
         const u32x4 rk = make_rsrc_words(kg + base_off, bytes);
         const u32x4 rv = make_rsrc_words(vg + base_off, bytes);
-        const uint32_t sk = lds_base + (uint32_t)((t & (STAGES - 1)) * STAGE_BYTES);
-        const uint32_t sv = sk + TILE_BYTES;
+        const uint32_t slot = (uint32_t)(t & (STAGES - 1)) * TILE_BYTES;
+        const uint32_t sk = lds_base + slot;
+        const uint32_t sv = lds_base + V_REGION + slot;
 #pragma unroll
         for (int j = 0; j < LDW; ++j) {
             const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane(wave * LDW + j);
@@ -168,107 +214,92 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     };
 
-    auto load_mask = [&](int t, float (&mv)[2][16]) __attribute__((always_inline)) {
+    const int key_base = kt_begin * BN;
+    auto half_k0 = [&](int u) __attribute__((always_inline)) { return key_base + HB * u; };
+
+    // mask values of half-tile u for this lane: keys half_k0(u) + 16 hh + 0..15.  Keys past sk
+    // read the next row (or zeros past the buffer): they are structurally masked anyway.
+    auto load_mask_half = [&](int u, MaskH& mh) __attribute__((always_inline)) {
         if constexpr (MASKED) {
-            const int64_t k0 = (int64_t)(kt_begin + t) * BN;
-            const bool tile_inside = k0 + BN <= p.sk && p.vec_mask;
+            const uint32_t off = mask_row_off + (uint32_t)(half_k0(u) + 16 * hh) * MESZ;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int jl = (int)k0 + 32 * sb + 16 * hh + 4 * c;
-                    const uint32_t off = mask_row_off + (uint32_t)jl * MESZ;
-                    float val[4];
-                    if (tile_inside) {
-                        if constexpr (MASKK == kMaskF32) {
-                            const f32x4 t4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rmask, off, 0, 0));
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) val[e] = t4[e];
-                        } else {
-                            const vec4 t4 = __builtin_bit_cast(vec4, __builtin_amdgcn_raw_buffer_load_b64(rmask, off, 0, 0));
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) val[e] = (float)t4[e];
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            val[e] = 0.0f;
-                            if (jl + e < p.sk) {
-                                if constexpr (MASKK == kMaskF32)
-                                    val[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rmask, off + 4u * e, 0, 0));
-                                else
-                                    val[e] = (float)__builtin_bit_cast(scalar, __builtin_amdgcn_raw_buffer_load_b16(rmask, off + 2u * e, 0, 0));
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) mv[sb][4 * c + e] = val[e];
-                }
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (MASKK == kMaskF32) mh.w[c] = vload_b128(rmask, off + 16u * c);
+                else mh.w[c] = vload_b64(rmask, off + 8u * c);
             }
         }
     };
+    auto mask_val = [&](const MaskH& mh, int v) __attribute__((always_inline)) -> float {
+        if constexpr (MASKK == kMaskF32) {
+            return __uint_as_float(mh.w[v >> 2][v & 3]);
+        } else if constexpr (MASKK == kMaskT) {
+            const uint32_t word = mh.w[v >> 2][(v >> 1) & 1];
+            const uint16_t bits = (uint16_t)((v & 1) ? (word >> 16) : (word & 0xffffu));
+            return (float)__builtin_bit_cast(scalar, bits);
+        } else {
+            return 0.0f;
+        }
+    };
 
+    // ---- wave-uniform half-tile ranges.  Half-tile u covers keys [half_k0(u), half_k0(u) + 31].
+    // active [ua, ub]: some row of the wave attends some key of it; full [fa, fb]: every row of
+    // the wave attends every key of it.  Both ranges are contiguous because lo and hi grow with
+    // the row.
     const int n_half = 2 * n_tiles;
-    // wave-uniform key bounds as 32-bit scalars (keys are < sk <= INT32_MAX)
     auto clamp32 = [](int64_t v) -> int { return (int)(v < -1 ? -1 : (v > 0x7fffffffLL ? 0x7fffffffLL : v)); };
     const int wlo_min = __builtin_amdgcn_readfirstlane(clamp32(w_lo_min));
     const int wlo_max = __builtin_amdgcn_readfirstlane(clamp32(w_lo_max));
     const int whi_min = __builtin_amdgcn_readfirstlane(clamp32(w_hi_min));
     const int whi_max = __builtin_amdgcn_readfirstlane(clamp32(w_hi_max));
     const bool wave_live = wave_has_rows && w_lo_min <= w_hi_max;
-    auto half_k0 = [&](int u) __attribute__((always_inline)) { return (kt_begin + (u >> 1)) * BN + HB * (u & 1); };
-    auto half_active = [&](int u) __attribute__((always_inline)) {
-        const int k0 = half_k0(u);
-        return wave_live && k0 <= whi_max && k0 + HB - 1 >= wlo_min;
-    };
-    auto half_full = [&](int u) __attribute__((always_inline)) {
-        const int k0 = half_k0(u);
-        return k0 >= wlo_max && k0 + HB - 1 <= whi_min;
-    };
-
-    // K operand reads: row 32*(u%2) + lr, chunk (2 ks + hh) ^ k_swz(lr) of ring slot (u/2) % 4
-    const uint32_t k_lane = (uint32_t)(lr * ROWB) ^ (uint32_t)(k_swz(lr) << 4);
-    auto qk = [&](int u, f32x16& acc) __attribute__((always_inline)) {
-        const char* kl = lds + ((u >> 1) & (STAGES - 1)) * STAGE_BYTES + HB * (u & 1) * ROWB;
-        acc = f32x16(0.0f);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const uint32_t off = k_lane ^ (uint32_t)((2 * ks + hh) << 4);
-            const vec8 a = *(const vec8*)(kl + off);
-            acc = Tr::mfma(a, qf[ks], acc);
-        }
-    };
-
-    // V operand reads through ds_read_b64_tr_b16.  Source lane l = 16 g + 4 k + c points at key
-    // 16*hh + 8*j + 4*r + k and dims 32*db + 16*(g%2) + 4*c .. +3 of the half-tile; the transpose
-    // hands lane l dims d = l % 32 of those four keys.
-    const int gq = (lane >> 4) & 1;
-    const int kq = (lane >> 2) & 3;
-    const int cq = lane & 3;
-    const uint32_t v_row = (uint32_t)((16 * hh + kq) * ROWB);
-    uint32_t v_col[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        const int lc = 4 * db + 2 * gq + (cq >> 1);
-        v_col[db] = v_row + (uint32_t)(((lc ^ v_swz(kq)) << 4) + 8 * (cq & 1));
+    int ua, ub, fa, fb;
+    {
+        auto fdiv = [](int64_t x) -> int64_t { return x >> 5; };      // floor(x / HB)
+        auto cdiv = [](int64_t x) -> int64_t { return -((-x) >> 5); };  // ceil(x / HB)
+        auto clip = [&](int64_t x) -> int { return (int)(x < -1 ? -1 : (x > n_half ? n_half : x)); };
+        static_assert(HB == 32, "fdiv/cdiv divide by 32");
+        int64_t a = cdiv((int64_t)wlo_min - (HB - 1) - key_base);
+        int64_t z = fdiv((int64_t)whi_max - key_base);
+        a = a < 0 ? 0 : a;
+        z = z > n_half - 1 ? n_half - 1 : z;
+        if (!wave_live) { a = 0; z = -1; }
+        ua = __builtin_amdgcn_readfirstlane(clip(a));
+        ub = __builtin_amdgcn_readfirstlane(clip(z));
+        fa = __builtin_amdgcn_readfirstlane(clip(cdiv((int64_t)wlo_max - key_base)));
+        fb = __builtin_amdgcn_readfirstlane(clip(fdiv((int64_t)whi_min - (HB - 1) - key_base)));
     }
-    auto pv = [&](int u, const vec8 (&pf)[2]) __attribute__((always_inline)) {
-        const char* vl = lds + ((u >> 1) & (STAGES - 1)) * STAGE_BYTES + TILE_BYTES + HB * (u & 1) * ROWB;
-        // all V^T fragments of the half-tile are requested before the first MFMA
-        vec8 vf[NDB][2];
+    // full(u) implies that the wave attends half-tile u: [fa, fb] lies inside [ua, ub]
+    auto full = [&](int u) __attribute__((always_inline)) { return u >= fa && u <= fb; };
+
+    // ---- LDS operand addresses: one per-lane base per operand; ring slot, half-tile, K slice and
+    // V block are immediates.
+    // K (A operand of S^T = K Q^T): lane (lr, hh) reads row lr, dims 16 ks + 8 hh .. +7.
+    const uint32_t k_base = (uint32_t)(lr * 32 + ((hh ^ ((lr >> 3) & 1)) << 4));
+    // V^T (A operand of O^T += V^T P^T) through ds_read_b64_tr_b16.  Source lane
+    // l = 16 g + 4 k + c points at key 16 hh + 8 j + 4 r + k and dims 32 db + 16 g + 4 c .. +3 of
+    // the half-tile (g = bit 4 of l, hh = bit 5); the transpose hands lane l dims d = l % 32 of
+    // those four keys.
+    const uint32_t v_base = (uint32_t)V_REGION + (uint32_t)((16 * hh + ((lane >> 2) & 3)) * 64 +
+                                                            ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
+    // slot_off: byte offset of the ring slot (wave-uniform); half_c: half-tile within the tile
+    auto read_k = [&](uint32_t slot_off, auto half_c, vec8 (&kf)[NKS]) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(half_c)::value * HB * ROWB;
+        const char* base = lds + slot_off + k_base;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const vec8*)(base + OFF + ks * 1024);
+    };
+    auto read_v = [&](uint32_t slot_off, auto half_c, vec8 (&vf)[NDB][2]) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(half_c)::value * HB * ROWB;
+        const char* base = lds + slot_off + v_base;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + v_col[db] + (8 * j) * ROWB));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + v_col[db] + (8 * j + 4) * ROWB));
+                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + OFF + db * 2048 + (8 * j) * 64));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + OFF + db * 2048 + (8 * j + 4) * 64));
                 vf[db][j] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = Tr::mfma(vf[db][j], pf[j], o[db]);
     };
 
     // score epilogue of one element: tracked units x (see RAW / SOFTCAP / MASKED)
@@ -292,9 +323,8 @@ fwd16_ring_kernel(const FwdParams p) {
     struct SoftmaxState {
         float mt, alpha, m_safe, nmk, lsum;
         bool moved;
-        f32x8 lo8, hi8;
     };
-    auto softmax_phase = [&](auto full_c, int ph, int u, f32x16& sc, const float (&mv)[16], vec8 (&pf)[2],
+    auto softmax_phase = [&](auto full_c, int ph, int u, f32x16& sc, const MaskH& mh, vec8 (&pf)[2],
                              SoftmaxState& st) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
         if (ph == 0 || ph == 1) {
@@ -305,7 +335,7 @@ fwd16_ring_kernel(const FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int v = 8 * ph + e;
-                float x = epi(sc[v], MASKED ? mv[v] : 0.0f);
+                float x = epi(sc[v], mask_val(mh, v));
                 if constexpr (!FULL) x = (v >= lo_rel && v <= hi_rel) ? x : neg_inf();
                 sc[v] = x;
                 st.mt = __builtin_fmaxf(st.mt, x);
@@ -327,12 +357,11 @@ fwd16_ring_kernel(const FwdParams p) {
                 float pv_;
                 if constexpr (SUB_FIRST) pv_ = exp2_hw((sc[v] - st.m_safe) * kfac);
                 else pv_ = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
-                if (v < 8) st.lo8[v] = pv_;
-                else st.hi8[v - 8] = pv_;
+                sc[v] = pv_;   // probabilities overwrite the scores
             }
         } else {
-            pf[0] = __builtin_convertvector(st.lo8, vec8);
-            pf[1] = __builtin_convertvector(st.hi8, vec8);
+            pf[0] = __builtin_convertvector(__builtin_shufflevector(sc, sc, 0, 1, 2, 3, 4, 5, 6, 7), vec8);
+            pf[1] = __builtin_convertvector(__builtin_shufflevector(sc, sc, 8, 9, 10, 11, 12, 13, 14, 15), vec8);
             float lsum = st.lsum;
 #pragma unroll
             for (int q = 0; q < 8; ++q)
@@ -341,88 +370,148 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     };
 
-    // Whole softmax of one half-tile (no MFMAs to overlap with).
-    auto softmax = [&](auto full_c, int u, f32x16& sc, const float (&mv)[16], vec8 (&pf)[2],
-                       bool& moved) __attribute__((always_inline)) -> float {
-        SoftmaxState st;
-#pragma unroll
-        for (int ph = 0; ph < 8; ++ph) softmax_phase(full_c, ph, u, sc, mv, pf, st);
-        moved = st.moved;
-        return st.alpha;
-    };
-
-    // S^T of half-tile u+1 on the matrix cores, with the softmax phases of half-tile u placed
-    // between its MFMAs (8 phases over NKS MFMAs).
-    auto fused = [&](int u, f32x16& sc, f32x16& sn, const float (&mv)[16], vec8 (&pf)[2],
-                     bool& moved) __attribute__((always_inline)) -> float {
-        const char* kl = lds + (((u + 1) >> 1) & (STAGES - 1)) * STAGE_BYTES + HB * ((u + 1) & 1) * ROWB;
-        SoftmaxState st;
-        // all K fragments of the half-tile are requested before the first MFMA
+    // ---- Pipelined block u: O^T += V^T P^T for half-tile u-1, the softmax of half-tile u
+    // (scores s_cur, probabilities into p_cur) and S^T = K Q^T for half-tile u+1 (into s_nxt).
+    // v_slot / k_slot: ring slots (byte offsets) of the tiles holding half-tile u-1's V and
+    // half-tile u+1's K; par_c = (u-1) % 2 = (u+1) % 2.  The rescale of O by the softmax's alpha
+    // follows the P.V products of half-tile u-1 and precedes those of half-tile u in the next
+    // block.
+    //
+    // Both products always run, so that every block has one MFMA sequence: P of a half-tile the
+    // wave does not attend is 0 (the masked softmax masks every element), which adds exactly 0
+    // because every V row in the ring is finite (rows past the cache length arrive as zeros),
+    // and scores of such a half-tile are masked away.  FULL: the softmax needs no structural
+    // mask.  WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
+    auto xbody = [&](auto full_c, auto with_pv_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
+                     f32x16& s_cur, f32x16& s_nxt, vec8 (&p_prev)[2], vec8 (&p_cur)[2], const MaskH& mh)
+                     __attribute__((always_inline)) {
+        constexpr bool WITH_PV = decltype(with_pv_c)::value;
+        constexpr int NPV = WITH_PV ? 2 * NDB : 0;
+        constexpr int NM = NPV + NKS;
+        vec8 vf[NDB][2];
+        if constexpr (WITH_PV) read_v(v_slot, par_c, vf);
         vec8 kf[NKS];
+        read_k(k_slot, par_c, kf);
+        SoftmaxState st;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const vec8*)(kl + (k_lane ^ (uint32_t)((2 * ks + hh) << 4)));
-        sn = f32x16(0.0f);
+        for (int i = 0; i < NM; ++i) {
+            if (i < NPV) {
+                const int j = i / NDB, db = i % NDB;
+                o[db] = Tr::mfma(vf[db][j], p_prev[j], o[db]);
+            } else {
+                const int ks = i - NPV;
+                s_nxt = Tr::mfma(kf[ks], qf[ks], ks == 0 ? f32x16(0.0f) : s_nxt);
+            }
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            sn = Tr::mfma(kf[ks], qf[ks], sn);
-#pragma unroll
-            for (int ph = ks * 8 / NKS; ph < (ks + 1) * 8 / NKS; ++ph)
-                softmax_phase(bool_c<true>{}, ph, u, sc, mv, pf, st);
+            for (int ph = i * 8 / NM; ph < (i + 1) * 8 / NM; ++ph) softmax_phase(full_c, ph, u, s_cur, mh, p_cur, st);
         }
-        moved = st.moved;
-        return st.alpha;
+        // Keep the probabilities and the row sum inside this block: otherwise they are sunk past
+        // the rescale branch below, next to the next block's P.V products that consume them,
+        // and no longer overlap this block's MFMAs.
+        {
+            u32x4 a = __builtin_bit_cast(u32x4, p_cur[0]), c = __builtin_bit_cast(u32x4, p_cur[1]);
+            asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run));
+            p_cur[0] = __builtin_bit_cast(vec8, a);
+            p_cur[1] = __builtin_bit_cast(vec8, c);
+        }
+        if (wave_any(st.moved)) {
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) o[i] *= st.alpha;
+        }
     };
 
-    auto substep = [&](int u, f32x16& sc, f32x16& sn, const float (&mc)[16]) __attribute__((always_inline)) {
-        const bool has_next = u + 1 < n_half;
-        const bool act_cur = half_active(u);
-        const bool act_nxt = has_next && half_active(u + 1);
-        vec8 pf[2];
-        bool moved = false;
-        float alpha = 1.0f;
-        if (act_cur && act_nxt && half_full(u)) {
-            alpha = fused(u, sc, sn, mc, pf, moved);
+    // ---- Ring schedule.  Slot t % 4 holds tile t.  Step t runs blocks 2t+1 and 2t+2: they read
+    // V of tile t and K of tile t+1, both landed before the step's barrier, and the step first
+    // starts the loads of tile t+3 into the slot tile t-1 used (free since the last barrier).
+    // Mask values: with head dim 64 those of the next step's two half-tiles are requested
+    // before that DMA, so the step's closing wait (everything but tile t+3) covers them; with
+    // head dim 128 (fewer free registers) the step requests its own before the DMA and waits
+    // for them (and tile t+2) right after it.
+    //
+    // Kinds of step: 0 skip (no half-tile of the step's blocks is attended by the wave: no
+    // compute, P = 0), 1 masked, 2 full (both blocks need no structural mask).  Steps go in
+    // pairs (2p, 2p+1) so that the mask buffers alternate statically; along p a wave's pairs
+    // run skip, masked, full, masked, skip, each kind in a loop of its own (no branch on the
+    // kind inside a loop, so the compiler keeps one register assignment per loop).
+    constexpr bool MASK_AHEAD = MASKED && DP == 64;
+    f32x16 s_even = f32x16(0.0f), s_odd = f32x16(0.0f);
+    vec8 p_even[2] = {vec8((scalar)0.0f), vec8((scalar)0.0f)};
+    vec8 p_odd[2] = {vec8((scalar)0.0f), vec8((scalar)0.0f)};
+    MaskH mask_a[2], mask_b[2];   // [half parity]: odd half-tile first
+    auto step = [&](auto kind_c, auto with_pv_c, int t, MaskH (&mcur)[2], MaskH (&mnext)[2]) __attribute__((always_inline)) {
+        constexpr int KIND = decltype(kind_c)::value;
+        if constexpr (MASK_AHEAD) {
+            load_mask_half(2 * t + 3, mnext[0]);
+            load_mask_half(2 * t + 4, mnext[1]);
+        } else if constexpr (MASKED) {
+            if constexpr (KIND != 0) {
+                load_mask_half(2 * t + 1, mcur[0]);
+                load_mask_half(2 * t + 2, mcur[1]);
+            }
+        }
+        issue_tile(t + 3);
+        if constexpr (KIND == 0) {
+            p_odd[0] = p_odd[1] = p_even[0] = p_even[1] = vec8((scalar)0.0f);
         } else {
-            if (act_cur) {
-                if (half_full(u)) alpha = softmax(bool_c<true>{}, u, sc, mc, pf, moved);
-                else alpha = softmax(bool_c<false>{}, u, sc, mc, pf, moved);
+            if constexpr (MASKED && !MASK_AHEAD) {
+                dma_wait<2 * LDW>();   // this step's mask values (and tile t+2) landed
+                launder(mcur[0]);
+                launder(mcur[1]);
             }
-            if (act_nxt) qk(u + 1, sn);
+            const uint32_t v_slot = (uint32_t)(t & (STAGES - 1)) * TILE_BYTES;
+            const uint32_t k_slot = (uint32_t)((t + 1) & (STAGES - 1)) * TILE_BYTES;
+            using F = bool_c<KIND == 2>;
+            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0]);
+            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1]);
         }
-        if (act_cur) {
-            if (wave_any(moved)) {
-#pragma unroll
-                for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-            }
-            pv(u, pf);
+        dma_wait<2 * LDW>();   // everything but tile t+3 landed
+        if constexpr (MASK_AHEAD) {
+            launder(mnext[0]);
+            launder(mnext[1]);
+        }
+        __syncthreads();
+    };
+    auto run_pairs = [&](auto kind_c, int p0, int p1) __attribute__((always_inline)) {
+        for (int pp = p0; pp < p1; ++pp) {
+            step(kind_c, bool_c<true>{}, 2 * pp, mask_a, mask_b);
+            step(kind_c, bool_c<true>{}, 2 * pp + 1, mask_b, mask_a);
         }
     };
 
-    // Ring schedule: slot t % 4 holds tile t.  Step t consumes tiles t (K rows 32..63, all of V)
-    // and t+1 (K rows 0..31) and starts the loads of tile t+3 into the slot tile t-1 used.
     if (n_tiles > 0) {
-        f32x16 sa, sb2;
-        float ma[2][16], mb[2][16];
-        load_mask(0, ma);
+        // pair p holds blocks 4p+1 .. 4p+4, which touch half-tiles 4p .. 4p+5
+        const int n_pairs = (n_tiles + 1) / 2;
+        int a0, a1, f0, f1;
+        {
+            auto fdiv4 = [](int64_t x) -> int64_t { return x >> 2; };
+            auto cdiv4 = [](int64_t x) -> int64_t { return -((-x) >> 2); };
+            auto clip = [&](int64_t x, int64_t lo, int64_t hi) -> int { return (int)(x < lo ? lo : (x > hi ? hi : x)); };
+            // not skip: 4p+5 >= ua and 4p <= ub
+            a0 = clip(cdiv4((int64_t)ua - 5), 0, n_pairs);
+            a1 = clip(fdiv4((int64_t)ub) + 1, a0, n_pairs);
+            // full: 4p+1 >= fa and 4p+4 <= fb
+            f0 = clip(cdiv4((int64_t)fa - 1), a0, a1);
+            f1 = clip(fdiv4((int64_t)fb - 4) + 1, f0, a1);
+            a0 = __builtin_amdgcn_readfirstlane(a0);
+            a1 = __builtin_amdgcn_readfirstlane(a1);
+            f0 = __builtin_amdgcn_readfirstlane(f0);
+            f1 = __builtin_amdgcn_readfirstlane(f1);
+        }
+        if constexpr (MASK_AHEAD) load_mask_half(0, mask_b[1]);
         issue_tile(0);
         issue_tile(1);
-        issue_tile(2);
-        dma_wait<2 * LDW>();   // tiles 0 and 1 landed; tile 2 may be in flight
+        dma_wait<2 * LDW>();   // tile 0 and the mask loads before it landed
+        if constexpr (MASK_AHEAD) launder(mask_b[1]);
         __syncthreads();
-        if (half_active(0)) qk(0, sa);
-        auto tile_step = [&](int t, float (&mc)[2][16], float (&mn)[2][16]) __attribute__((always_inline)) {
-            if (t + 1 < n_tiles) load_mask(t + 1, mn);
-            issue_tile(t + 3);
-            substep(2 * t, sa, sb2, mc[0]);
-            substep(2 * t + 1, sb2, sa, mc[1]);
-            dma_wait<2 * LDW>();   // everything but tile t+3 landed
-            __syncthreads();
-        };
-        for (int t = 0; t < n_tiles; t += 2) {
-            tile_step(t, ma, mb);
-            if (t + 1 < n_tiles) tile_step(t + 1, mb, ma);
-        }
+        // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
+        step(int_c<1>{}, bool_c<false>{}, -1, mask_b, mask_a);
+        run_pairs(int_c<0>{}, 0, a0);
+        run_pairs(int_c<1>{}, a0, f0);
+        run_pairs(int_c<2>{}, f0, f1);
+        run_pairs(int_c<1>{}, f1, a1);
+        run_pairs(int_c<0>{}, a1, n_pairs);
     }
+    dma_wait<0>();   // the ring's trailing (empty) tile loads retire before the workgroup ends
 
     const float l = half_swap_sum(l_run);
     if (!row_valid) return;
