@@ -131,24 +131,28 @@ fwd16_ring_kernel(const FwdParams p) {
     const char* kg = (const char*)p.k + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
     const char* vg = (const char*)p.v + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
 
-    // ---- Q fragments: lane (m, hh) holds Q[row][16*ks + 8*hh .. +7]
+    // ---- Q fragments: lane (m, hh) holds Q[row][16*ks + 8*hh .. +7].  The loads go through
+    // inline asm like the K/V ring, so the first ring wait retires them together with the first
+    // tile (the two latencies overlap), and the tile loop holds no register the compiler sees as
+    // loaded from memory (its wait-count pass would otherwise drain the ring inside the loop).
     vec8 qf[NKS];
     {
         const scalar* qrow = qg + (((int64_t)b * p.heads + h) * p.sq + (row_valid ? row : 0)) * D;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qf[ks] = row_valid ? *(const vec8*)(qrow + 16 * ks + 8 * hh) : vec8((scalar)0.0f);
-        // Retire the Q loads here and hand the fragments on through an empty asm: the tile loop
-        // then holds no register the compiler sees as loaded from memory, so its wait-count
-        // pass never drains the K/V ring inside the loop.
-        dma_wait<0>();
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 t;
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(t) : "v"(qrow + 16 * ks + 8 * hh));
+            qf[ks] = __builtin_bit_cast(vec8, t);
+        }
+    }
+    auto launder_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             u32x4 t = __builtin_bit_cast(u32x4, qf[ks]);
             asm volatile("" : "+v"(t));
-            qf[ks] = __builtin_bit_cast(vec8, t);
+            qf[ks] = row_valid ? __builtin_bit_cast(vec8, t) : vec8((scalar)0.0f);
         }
-    }
+    };
 
     // ---- mask rows of this workgroup (rows are 16-byte aligned: the dispatcher checks it)
     constexpr uint32_t MESZ = MASKK == kMaskF32 ? 4u : 2u;
@@ -393,6 +397,20 @@ fwd16_ring_kernel(const FwdParams p) {
         vec8 kf[NKS];
         read_k(k_slot, par_c, kf);
         SoftmaxState st;
+        // Instruction order of the block: every LDS operand read first (their latency then
+        // overlaps the maximum phase and the first MFMAs), then one MFMA per group of VALU_PER
+        // softmax instructions.
+        constexpr bool FULL_ = decltype(full_c)::value;
+        constexpr int VALU_EST = 72 + (RAW ? 0 : 16) + (SUB_FIRST ? 16 : 0) + (MASKK == kMaskT ? 24 : 0) +
+                                 (SOFTCAP ? 160 : 0) + (FULL_ ? 0 : 44);
+        constexpr int VALU_PER = (VALU_EST - 8 + NM - 1) / NM;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (WITH_PV ? 4 * NDB : 0) + NKS, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_PER, 0);
+        }
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             if (i < NPV) {
@@ -500,7 +518,8 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (MASK_AHEAD) load_mask_half(0, mask_b[1]);
         issue_tile(0);
         issue_tile(1);
-        dma_wait<2 * LDW>();   // tile 0 and the mask loads before it landed
+        dma_wait<2 * LDW>();   // Q, tile 0 and the mask loads before it landed
+        launder_q();
         if constexpr (MASK_AHEAD) launder(mask_b[1]);
         __syncthreads();
         // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
