@@ -39,6 +39,45 @@ namespace fa {
 template <int N>
 using int_c = std::integral_constant<int, N>;
 
+// f(int_c<I>{}) for I in [B, E), unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(int_c<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// LDS operand reads through inline asm: the kernel orders them and places their waits itself
+// (lds_wait), so that each MFMA waits for its own operands only.  Results must not be read
+// before the lds_wait that covers them.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr_b64(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// Wait until at most N LDS operations of this wave are in flight (they retire in order), then
+// hand `x` on as a value defined after the wait.
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T& x) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T& x, T& y) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
+}
+
 // Mask values of one half-tile for one lane (16 keys), exactly as loaded: fp32 words, or
 // 16-bit values packed two per word.
 template <int MASKK> struct MaskHalf {};
@@ -392,37 +431,54 @@ fwd16_ring_kernel(const FwdParams p) {
         constexpr bool WITH_PV = decltype(with_pv_c)::value;
         constexpr int NPV = WITH_PV ? 2 * NDB : 0;
         constexpr int NM = NPV + NKS;
-        vec8 vf[NDB][2];
-        if constexpr (WITH_PV) read_v(v_slot, par_c, vf);
-        vec8 kf[NKS];
-        read_k(k_slot, par_c, kf);
-        SoftmaxState st;
-        // Instruction order of the block: every LDS operand read first (their latency then
-        // overlaps the maximum phase and the first MFMAs), then one MFMA per group of VALU_PER
-        // softmax instructions.
-        constexpr bool FULL_ = decltype(full_c)::value;
-        constexpr int VALU_EST = 72 + (RAW ? 0 : 16) + (SUB_FIRST ? 16 : 0) + (MASKK == kMaskT ? 24 : 0) +
-                                 (SOFTCAP ? 160 : 0) + (FULL_ ? 0 : 44);
-        constexpr int VALU_PER = (VALU_EST - 8 + NM - 1) / NM;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (WITH_PV ? 4 * NDB : 0) + NKS, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_PER, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            if (i < NPV) {
-                const int j = i / NDB, db = i % NDB;
-                o[db] = Tr::mfma(vf[db][j], p_prev[j], o[db]);
+        // LDS operand reads, in the order the MFMAs consume them: read r < 2*NPV is half r % 2
+        // of P.V MFMA r / 2 (V^T, 4 keys x 4 dims per transpose read), read 2*NPV + ks is the K
+        // fragment of Q.K MFMA ks.  Reads run AHEAD operands in front of the MFMA that needs
+        // them; each MFMA waits for its own.
+        constexpr int NR = 2 * NPV + NKS;
+        constexpr int AHEAD = 12;
+        constexpr int OFFH = decltype(par_c)::value * HB * ROWB;
+        const uint32_t va = (uint32_t)(uintptr_t)(lds + v_slot) + v_base;
+        const uint32_t ka = (uint32_t)(uintptr_t)(lds + k_slot) + k_base;
+        u32x2 rv[NPV > 0 ? 2 * NPV : 1];
+        u32x4 rk[NKS];
+        auto issue = [&](auto r_c) __attribute__((always_inline)) {
+            constexpr int r = decltype(r_c)::value;
+            if constexpr (r < 2 * NPV) {
+                constexpr int m = r / 2, hv = r % 2, j = m / NDB, db = m % NDB;
+                rv[r] = lds_read_tr_b64<OFFH + db * 2048 + (8 * j + 4 * hv) * 64>(va);
             } else {
-                const int ks = i - NPV;
-                s_nxt = Tr::mfma(kf[ks], qf[ks], ks == 0 ? f32x16(0.0f) : s_nxt);
+                constexpr int ks = r - 2 * NPV;
+                rk[ks] = lds_read_b128<OFFH + ks * 1024>(ka);
+            }
+        };
+        static_for<0, (NR < AHEAD ? NR : AHEAD)>(issue);
+        SoftmaxState st;
+        static_for<0, NM>([&](auto m_c) __attribute__((always_inline)) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int last = m < NPV ? 2 * m + 1 : NPV + m;   // last read MFMA m needs
+            constexpr int upto = last + 1 + AHEAD < NR ? last + 1 + AHEAD : NR;
+            constexpr int before = (m == 0 ? 0 : ((m - 1 < NPV ? 2 * (m - 1) + 1 : NPV + m - 1) + 1 + AHEAD));
+            constexpr int from = (m == 0 ? (NR < AHEAD ? NR : AHEAD) : (before < NR ? before : NR));
+            static_for<from, upto>(issue);
+            constexpr int in_flight = upto - (last + 1);
+            if constexpr (m < NPV) {
+                constexpr int j = m / NDB, db = m % NDB;
+                lds_wait<in_flight>(rv[2 * m], rv[2 * m + 1]);
+                const u32x4 a = u32x4{rv[2 * m][0], rv[2 * m][1], rv[2 * m + 1][0], rv[2 * m + 1][1]};
+                o[db] = Tr::mfma(__builtin_bit_cast(vec8, a), p_prev[j], o[db]);
+            } else {
+                constexpr int ks = m - NPV;
+                u32x4 a = rk[ks];
+                lds_wait<in_flight>(a);
+                s_nxt = Tr::mfma(__builtin_bit_cast(vec8, a), qf[ks], ks == 0 ? f32x16(0.0f) : s_nxt);
             }
 #pragma unroll
-            for (int ph = i * 8 / NM; ph < (i + 1) * 8 / NM; ++ph) softmax_phase(full_c, ph, u, s_cur, mh, p_cur, st);
-        }
+            for (int ph = m * 8 / NM; ph < (m + 1) * 8 / NM; ++ph) softmax_phase(full_c, ph, u, s_cur, mh, p_cur, st);
+            // units (reads, wait, MFMA, softmax phase) stay in this order: a later unit's wait
+            // must not run ahead of this unit's MFMA
+            __builtin_amdgcn_sched_barrier(0);
+        });
         // Keep the probabilities and the row sum inside this block: otherwise they are sunk past
         // the rescale branch below, next to the next block's P.V products that consume them,
         // and no longer overlap this block's MFMAs.
