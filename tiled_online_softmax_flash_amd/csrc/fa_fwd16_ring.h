@@ -48,36 +48,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// LDS operand reads through inline asm: the kernel orders them and places their waits itself
-// (lds_wait), so that each MFMA waits for its own operands only.  Results must not be read
-// before the lds_wait that covers them.
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr_b64(uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-// Wait until at most N LDS operations of this wave are in flight (they retire in order), then
-// hand `x` on as a value defined after the wait.
-template <int N, typename T>
-__device__ __forceinline__ void lds_wait(T& x) {
-    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
-}
-template <int N, typename T>
-__device__ __forceinline__ void lds_wait(T& x, T& y) {
-    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
-}
-
 // Mask values of one half-tile for one lane (16 keys), exactly as loaded: fp32 words, or
 // 16-bit values packed two per word.
 template <int MASKK> struct MaskHalf {};
@@ -106,8 +76,9 @@ __device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
     }
 }
 
-template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW, int RB>
+__global__ void __attribute__((amdgpu_flat_work_group_size(ring_threads(RB), ring_threads(RB)),
+                               amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
 fwd16_ring_kernel(const FwdParams p) {
     using vec8 = typename Tr::vec8;
     using vec4 = typename Tr::vec4;
@@ -115,7 +86,8 @@ fwd16_ring_kernel(const FwdParams p) {
     using scalar = typename Tr::scalar;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    constexpr int WAVES = 8;
+    constexpr int WAVES = ring_threads(RB) / 64;
+    constexpr int WROWS = kWaveRows * RB;        // query rows per wave: RB blocks of 32
     constexpr int BN = 64, HB = 32, STAGES = 4;
     constexpr int ROWB = DP * 2;                 // bytes per K/V row
     constexpr int CPR = DP / 8;                  // 16-byte chunks per row
@@ -124,7 +96,6 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int LDW = TILE_BYTES / 1024 / WAVES;  // 1 KiB DMA ops per wave per operand per tile
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
-    constexpr int NMF = 2 * NDB + NKS;           // MFMAs per pipelined block
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
     using MaskH = MaskHalf<MASKK>;
@@ -150,15 +121,22 @@ fwd16_ring_kernel(const FwdParams p) {
     const KeyRule rule = make_rule(p, b);
     const int64_t q0 = (int64_t)w.qt * kRingBlockRows;
     const int64_t q_last = (q0 + kRingBlockRows < p.sq ? q0 + kRingBlockRows : p.sq) - 1;
-    const int64_t wr0 = q0 + wave * kWaveRows;
+    const int64_t wr0 = q0 + wave * WROWS;
     const bool wave_has_rows = wr0 < p.sq;
-    const int64_t wr1 = (wr0 + kWaveRows - 1 < p.sq ? wr0 + kWaveRows - 1 : p.sq - 1);
-    const int64_t row = wr0 + lr;
-    const bool row_valid = row < p.sq;
-    const int64_t my_lo = row_valid ? rule.lo(row) : 1;
-    const int64_t my_hi = row_valid ? rule.hi(row) : 0;
-    const int my_lo32 = (int)(my_lo < 0x7fffffffLL ? my_lo : 0x7fffffffLL);
-    const int my_hi32 = (int)(my_hi > -1 ? my_hi : -1);
+    const int64_t wr1 = (wr0 + WROWS - 1 < p.sq ? wr0 + WROWS - 1 : p.sq - 1);
+    // row block rb of the wave: rows wr0 + 32 rb + (0..31); lane (lr, hh) owns row wr0 + 32 rb + lr
+    int64_t row[RB];
+    bool row_valid[RB];
+    int my_lo32[RB], my_hi32[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        row[rb] = wr0 + 32 * rb + lr;
+        row_valid[rb] = row[rb] < p.sq;
+        const int64_t lo = row_valid[rb] ? rule.lo(row[rb]) : 1;
+        const int64_t hi = row_valid[rb] ? rule.hi(row[rb]) : 0;
+        my_lo32[rb] = (int)(lo < 0x7fffffffLL ? lo : 0x7fffffffLL);
+        my_hi32[rb] = (int)(hi > -1 ? hi : -1);
+    }
     const int64_t w_lo_min = rule.lo(wr0), w_lo_max = rule.lo(wr1);
     const int64_t w_hi_min = rule.hi(wr0), w_hi_max = rule.hi(wr1);
 
@@ -174,41 +152,52 @@ fwd16_ring_kernel(const FwdParams p) {
     // inline asm like the K/V ring, so the first ring wait retires them together with the first
     // tile (the two latencies overlap), and the tile loop holds no register the compiler sees as
     // loaded from memory (its wait-count pass would otherwise drain the ring inside the loop).
-    vec8 qf[NKS];
-    {
-        const scalar* qrow = qg + (((int64_t)b * p.heads + h) * p.sq + (row_valid ? row : 0)) * D;
+    vec8 qf[RB][NKS];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const scalar* qrow = qg + (((int64_t)b * p.heads + h) * p.sq + (row_valid[rb] ? row[rb] : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             u32x4 t;
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(t) : "v"(qrow + 16 * ks + 8 * hh));
-            qf[ks] = __builtin_bit_cast(vec8, t);
+            qf[rb][ks] = __builtin_bit_cast(vec8, t);
         }
     }
     auto launder_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4 t = __builtin_bit_cast(u32x4, qf[ks]);
-            asm volatile("" : "+v"(t));
-            qf[ks] = row_valid ? __builtin_bit_cast(vec8, t) : vec8((scalar)0.0f);
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4 t = __builtin_bit_cast(u32x4, qf[rb][ks]);
+                asm volatile("" : "+v"(t));
+                qf[rb][ks] = row_valid[rb] ? __builtin_bit_cast(vec8, t) : vec8((scalar)0.0f);
+            }
         }
     };
 
     // ---- mask rows of this workgroup (rows are 16-byte aligned: the dispatcher checks it)
     constexpr uint32_t MESZ = MASKK == kMaskF32 ? 4u : 2u;
     u32x4 rmask = u32x4{0u, 0u, 0u, 0u};
-    uint32_t mask_row_off = 0;
+    uint32_t mask_row_off[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mask_row_off[rb] = 0;
     if constexpr (MASKED) {
         const int64_t rows_here = q_last - q0 + 1;
         const char* mbase = (const char*)p.mask + ((mask_plane(p, b, h) * p.sq + q0) * (int64_t)p.sk) * MESZ;
         rmask = make_rsrc_words(mbase, (int)(rows_here * p.sk * MESZ));
-        mask_row_off = (uint32_t)((row - q0) * (int64_t)p.sk) * MESZ;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mask_row_off[rb] = (uint32_t)((row[rb] - q0) * (int64_t)p.sk) * MESZ;
     }
 
-    f32x16 o[NDB];
+    f32x16 o[RB][NDB];
+    float m_run[RB], l_run[RB];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) o[i] = f32x16(0.0f);
-    float m_run = neg_inf();
-    float l_run = 0.0f;
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) o[rb][i] = f32x16(0.0f);
+        m_run[rb] = neg_inf();
+        l_run[rb] = 0.0f;
+    }
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
@@ -262,15 +251,22 @@ fwd16_ring_kernel(const FwdParams p) {
 
     // mask values of half-tile u for this lane: keys half_k0(u) + 16 hh + 0..15.  Keys past sk
     // read the next row (or zeros past the buffer): they are structurally masked anyway.
-    auto load_mask_half = [&](int u, MaskH& mh) __attribute__((always_inline)) {
+    auto load_mask_half = [&](int u, MaskH (&mh)[RB]) __attribute__((always_inline)) {
         if constexpr (MASKED) {
-            const uint32_t off = mask_row_off + (uint32_t)(half_k0(u) + 16 * hh) * MESZ;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if constexpr (MASKK == kMaskF32) mh.w[c] = vload_b128(rmask, off + 16u * c);
-                else mh.w[c] = vload_b64(rmask, off + 8u * c);
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint32_t off = mask_row_off[rb] + (uint32_t)(half_k0(u) + 16 * hh) * MESZ;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (MASKK == kMaskF32) mh[rb].w[c] = vload_b128(rmask, off + 16u * c);
+                    else mh[rb].w[c] = vload_b64(rmask, off + 8u * c);
+                }
             }
         }
+    };
+    auto launder_mask = [&](MaskH (&mh)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) launder(mh[rb]);
     };
     auto mask_val = [&](const MaskH& mh, int v) __attribute__((always_inline)) -> float {
         if constexpr (MASKK == kMaskF32) {
@@ -324,27 +320,6 @@ fwd16_ring_kernel(const FwdParams p) {
     // those four keys.
     const uint32_t v_base = (uint32_t)V_REGION + (uint32_t)((16 * hh + ((lane >> 2) & 3)) * 64 +
                                                             ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
-    // slot_off: byte offset of the ring slot (wave-uniform); half_c: half-tile within the tile
-    auto read_k = [&](uint32_t slot_off, auto half_c, vec8 (&kf)[NKS]) __attribute__((always_inline)) {
-        constexpr int OFF = decltype(half_c)::value * HB * ROWB;
-        const char* base = lds + slot_off + k_base;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const vec8*)(base + OFF + ks * 1024);
-    };
-    auto read_v = [&](uint32_t slot_off, auto half_c, vec8 (&vf)[NDB][2]) __attribute__((always_inline)) {
-        constexpr int OFF = decltype(half_c)::value * HB * ROWB;
-        const char* base = lds + slot_off + v_base;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + OFF + db * 2048 + (8 * j) * 64));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + OFF + db * 2048 + (8 * j + 4) * 64));
-                vf[db][j] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-        }
-    };
-
     // score epilogue of one element: tracked units x (see RAW / SOFTCAP / MASKED)
     auto epi = [&](float sv, float mvv) __attribute__((always_inline)) -> float {
         if constexpr (SOFTCAP) {
@@ -367,13 +342,14 @@ fwd16_ring_kernel(const FwdParams p) {
         float mt, alpha, m_safe, nmk, lsum;
         bool moved;
     };
-    auto softmax_phase = [&](auto full_c, int ph, int u, f32x16& sc, const MaskH& mh, vec8 (&pf)[2],
+    auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, vec8 (&pf)[2],
                              SoftmaxState& st) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
+        constexpr int rb = decltype(rb_c)::value;
         if (ph == 0 || ph == 1) {
             const int base = half_k0(u) + 16 * hh;
-            const int lo_rel = my_lo32 - base;
-            const int hi_rel = my_hi32 - base;
+            const int lo_rel = my_lo32[rb] - base;
+            const int hi_rel = my_hi32[rb] - base;
             if (ph == 0) st.mt = neg_inf();
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -385,14 +361,14 @@ fwd16_ring_kernel(const FwdParams p) {
             }
         } else if (ph == 2) {
             const float mt = half_swap_max(st.mt);
-            const bool need = mt > m_run + th_x;
-            const float m_new = need ? mt : m_run;
-            st.alpha = need ? exp2_hw((m_run - m_new) * kfac) : 1.0f;
+            const bool need = mt > m_run[rb] + th_x;
+            const float m_new = need ? mt : m_run[rb];
+            st.alpha = need ? exp2_hw((m_run[rb] - m_new) * kfac) : 1.0f;
             st.moved = need;
-            m_run = m_new;
-            st.m_safe = (m_run == neg_inf()) ? 0.0f : m_run;
+            m_run[rb] = m_new;
+            st.m_safe = (m_new == neg_inf()) ? 0.0f : m_new;
             st.nmk = -st.m_safe * kfac;
-            st.lsum = l_run * st.alpha;
+            st.lsum = l_run[rb] * st.alpha;
         } else if (ph <= 6) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -409,88 +385,99 @@ fwd16_ring_kernel(const FwdParams p) {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 lsum = Tr::sum2(vec2{pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]}, lsum);
-            l_run = lsum;
+            l_run[rb] = lsum;
         }
     };
 
     // ---- Pipelined block u: O^T += V^T P^T for half-tile u-1, the softmax of half-tile u
-    // (scores s_cur, probabilities into p_cur) and S^T = K Q^T for half-tile u+1 (into s_nxt).
-    // v_slot / k_slot: ring slots (byte offsets) of the tiles holding half-tile u-1's V and
-    // half-tile u+1's K; par_c = (u-1) % 2 = (u+1) % 2.  The rescale of O by the softmax's alpha
-    // follows the P.V products of half-tile u-1 and precedes those of half-tile u in the next
-    // block.
+    // (scores s_cur, probabilities into p_cur) and S^T = K Q^T for half-tile u+1 (into s_nxt),
+    // for each of the wave's RB row blocks; every K/V operand fragment read from LDS feeds the RB
+    // row blocks' MFMAs back to back.  v_slot / k_slot: ring slots (byte offsets) of the tiles
+    // holding half-tile u-1's V and half-tile u+1's K; par_c = (u-1) % 2 = (u+1) % 2.  The rescale
+    // of O by the softmax's alpha follows the P.V products of half-tile u-1 and precedes those of
+    // half-tile u in the next block.
     //
-    // Both products always run, so that every block has one MFMA sequence: P of a half-tile the
-    // wave does not attend is 0 (the masked softmax masks every element), which adds exactly 0
-    // because every V row in the ring is finite (rows past the cache length arrive as zeros),
-    // and scores of such a half-tile are masked away.  FULL: the softmax needs no structural
-    // mask.  WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
+    // Both products always run, so that every block has one MFMA sequence: P of a half-tile a row
+    // block does not attend is 0 (the masked softmax masks every element), which adds exactly 0
+    // because every V row in the ring is finite (rows past the cache length arrive as zeros), and
+    // scores of such a half-tile are masked away.  FULL: the softmax needs no structural mask.
+    // WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
     auto xbody = [&](auto full_c, auto with_pv_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
-                     f32x16& s_cur, f32x16& s_nxt, vec8 (&p_prev)[2], vec8 (&p_cur)[2], const MaskH& mh)
-                     __attribute__((always_inline)) {
+                     f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], vec8 (&p_prev)[RB][2], vec8 (&p_cur)[RB][2],
+                     const MaskH (&mh)[RB]) __attribute__((always_inline)) {
         constexpr bool WITH_PV = decltype(with_pv_c)::value;
-        constexpr int NPV = WITH_PV ? 2 * NDB : 0;
-        constexpr int NM = NPV + NKS;
+        constexpr int NPV = WITH_PV ? 2 * NDB : 0;   // V^T fragments (one per P.V MFMA per row block)
+        constexpr int NF = NPV + NKS;                // operand fragments of the block
+        constexpr int NM = RB * NF;                  // MFMAs of the block
         // LDS operand reads, in the order the MFMAs consume them: read r < 2*NPV is half r % 2
-        // of P.V MFMA r / 2 (V^T, 4 keys x 4 dims per transpose read), read 2*NPV + ks is the K
-        // fragment of Q.K MFMA ks.  Reads run AHEAD operands in front of the MFMA that needs
-        // them; each MFMA waits for its own.
+        // of V^T fragment r / 2 (4 keys x 4 dims per transpose read), read 2*NPV + ks is K
+        // fragment ks.  Reads run AHEAD operands in front of the first MFMA that needs them
+        // (the compiler's waits then let each MFMA wait for its own reads only).
         constexpr int NR = 2 * NPV + NKS;
         constexpr int AHEAD = 12;
         constexpr int OFFH = decltype(par_c)::value * HB * ROWB;
-        const uint32_t va = (uint32_t)(uintptr_t)(lds + v_slot) + v_base;
-        const uint32_t ka = (uint32_t)(uintptr_t)(lds + k_slot) + k_base;
         u32x2 rv[NPV > 0 ? 2 * NPV : 1];
         u32x4 rk[NKS];
         auto issue = [&](auto r_c) __attribute__((always_inline)) {
             constexpr int r = decltype(r_c)::value;
             if constexpr (r < 2 * NPV) {
-                constexpr int m = r / 2, hv = r % 2, j = m / NDB, db = m % NDB;
-                rv[r] = lds_read_tr_b64<OFFH + db * 2048 + (8 * j + 4 * hv) * 64>(va);
+                constexpr int f = r / 2, hv = r % 2, j = f / NDB, db = f % NDB;
+                rv[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(lds + v_slot + v_base + (OFFH + db * 2048 + (8 * j + 4 * hv) * 64))));
             } else {
                 constexpr int ks = r - 2 * NPV;
-                rk[ks] = lds_read_b128<OFFH + ks * 1024>(ka);
+                rk[ks] = *(const u32x4*)(lds + k_slot + k_base + (OFFH + ks * 1024));
             }
         };
         static_for<0, (NR < AHEAD ? NR : AHEAD)>(issue);
-        SoftmaxState st;
+        SoftmaxState st[RB];
+        u32x4 frag = u32x4{0u, 0u, 0u, 0u};
         static_for<0, NM>([&](auto m_c) __attribute__((always_inline)) {
             constexpr int m = decltype(m_c)::value;
-            constexpr int last = m < NPV ? 2 * m + 1 : NPV + m;   // last read MFMA m needs
-            constexpr int upto = last + 1 + AHEAD < NR ? last + 1 + AHEAD : NR;
-            constexpr int before = (m == 0 ? 0 : ((m - 1 < NPV ? 2 * (m - 1) + 1 : NPV + m - 1) + 1 + AHEAD));
-            constexpr int from = (m == 0 ? (NR < AHEAD ? NR : AHEAD) : (before < NR ? before : NR));
-            static_for<from, upto>(issue);
-            constexpr int in_flight = upto - (last + 1);
-            if constexpr (m < NPV) {
-                constexpr int j = m / NDB, db = m % NDB;
-                lds_wait<in_flight>(rv[2 * m], rv[2 * m + 1]);
-                const u32x4 a = u32x4{rv[2 * m][0], rv[2 * m][1], rv[2 * m + 1][0], rv[2 * m + 1][1]};
-                o[db] = Tr::mfma(__builtin_bit_cast(vec8, a), p_prev[j], o[db]);
-            } else {
-                constexpr int ks = m - NPV;
-                u32x4 a = rk[ks];
-                lds_wait<in_flight>(a);
-                s_nxt = Tr::mfma(__builtin_bit_cast(vec8, a), qf[ks], ks == 0 ? f32x16(0.0f) : s_nxt);
+            constexpr int f = m / RB, rb = m % RB;
+            if constexpr (rb == 0) {
+                constexpr int last = f < NPV ? 2 * f + 1 : NPV + f;   // last read fragment f needs
+                constexpr int prev = f == 0 ? -1 : (f - 1 < NPV ? 2 * (f - 1) + 1 : NPV + f - 1);
+                constexpr int top = NR < AHEAD ? NR : AHEAD;
+                constexpr int from = f == 0 ? top : (prev + 1 + AHEAD < NR ? prev + 1 + AHEAD : NR);
+                constexpr int upto = last + 1 + AHEAD < NR ? last + 1 + AHEAD : NR;
+                static_for<(from < upto ? from : upto), upto>(issue);
+                if constexpr (f < NPV) frag = u32x4{rv[2 * f][0], rv[2 * f][1], rv[2 * f + 1][0], rv[2 * f + 1][1]};
+                else frag = rk[f - NPV];
             }
-#pragma unroll
-            for (int ph = m * 8 / NM; ph < (m + 1) * 8 / NM; ++ph) softmax_phase(full_c, ph, u, s_cur, mh, p_cur, st);
-            // units (reads, wait, MFMA, softmax phase) stay in this order: a later unit's wait
+            if constexpr (f < NPV) {
+                constexpr int j = f / NDB, db = f % NDB;
+                o[rb][db] = Tr::mfma(__builtin_bit_cast(vec8, frag), p_prev[rb][j], o[rb][db]);
+            } else {
+                constexpr int ks = f - NPV;
+                s_nxt[rb] = Tr::mfma(__builtin_bit_cast(vec8, frag), qf[rb][ks], ks == 0 ? f32x16(0.0f) : s_nxt[rb]);
+            }
+            // softmax phases of the RB row blocks, interleaved (slot q: phase q / RB of row block q % RB)
+            static_for<m * 8 * RB / NM, (m + 1) * 8 * RB / NM>([&](auto q_c) __attribute__((always_inline)) {
+                constexpr int q = decltype(q_c)::value;
+                constexpr int srb = q % RB;
+                softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb]);
+            });
+            // units (reads, wait, MFMA, softmax phases) stay in this order: a later unit's wait
             // must not run ahead of this unit's MFMA
             __builtin_amdgcn_sched_barrier(0);
         });
-        // Keep the probabilities and the row sum inside this block: otherwise they are sunk past
-        // the rescale branch below, next to the next block's P.V products that consume them,
-        // and no longer overlap this block's MFMAs.
-        {
-            u32x4 a = __builtin_bit_cast(u32x4, p_cur[0]), c = __builtin_bit_cast(u32x4, p_cur[1]);
-            asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run));
-            p_cur[0] = __builtin_bit_cast(vec8, a);
-            p_cur[1] = __builtin_bit_cast(vec8, c);
-        }
-        if (wave_any(st.moved)) {
 #pragma unroll
-            for (int i = 0; i < NDB; ++i) o[i] *= st.alpha;
+        for (int rb = 0; rb < RB; ++rb) {
+            // Keep the probabilities and the row sum inside this block: otherwise they are sunk
+            // past the rescale branch below, next to the next block's P.V products that consume
+            // them, and no longer overlap this block's MFMAs.
+            u32x4 a = __builtin_bit_cast(u32x4, p_cur[rb][0]), c = __builtin_bit_cast(u32x4, p_cur[rb][1]);
+            asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run[rb]));
+            p_cur[rb][0] = __builtin_bit_cast(vec8, a);
+            p_cur[rb][1] = __builtin_bit_cast(vec8, c);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            if (wave_any(st[rb].moved)) {
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) o[rb][i] *= st[rb].alpha;
+            }
         }
     };
 
@@ -508,11 +495,15 @@ fwd16_ring_kernel(const FwdParams p) {
     // run skip, masked, full, masked, skip, each kind in a loop of its own (no branch on the
     // kind inside a loop, so the compiler keeps one register assignment per loop).
     constexpr bool MASK_AHEAD = MASKED && DP == 64;
-    f32x16 s_even = f32x16(0.0f), s_odd = f32x16(0.0f);
-    vec8 p_even[2] = {vec8((scalar)0.0f), vec8((scalar)0.0f)};
-    vec8 p_odd[2] = {vec8((scalar)0.0f), vec8((scalar)0.0f)};
-    MaskH mask_a[2], mask_b[2];   // [half parity]: odd half-tile first
-    auto step = [&](auto kind_c, auto with_pv_c, int t, MaskH (&mcur)[2], MaskH (&mnext)[2]) __attribute__((always_inline)) {
+    f32x16 s_even[RB], s_odd[RB];
+    vec8 p_even[RB][2], p_odd[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        s_even[rb] = s_odd[rb] = f32x16(0.0f);
+        p_even[rb][0] = p_even[rb][1] = p_odd[rb][0] = p_odd[rb][1] = vec8((scalar)0.0f);
+    }
+    MaskH mask_a[2][RB], mask_b[2][RB];   // [half parity][row block]: odd half-tile first
+    auto step = [&](auto kind_c, auto with_pv_c, int t, MaskH (&mcur)[2][RB], MaskH (&mnext)[2][RB]) __attribute__((always_inline)) {
         constexpr int KIND = decltype(kind_c)::value;
         if constexpr (MASK_AHEAD) {
             load_mask_half(2 * t + 3, mnext[0]);
@@ -525,12 +516,14 @@ fwd16_ring_kernel(const FwdParams p) {
         }
         issue_tile(t + 3);
         if constexpr (KIND == 0) {
-            p_odd[0] = p_odd[1] = p_even[0] = p_even[1] = vec8((scalar)0.0f);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = vec8((scalar)0.0f);
         } else {
             if constexpr (MASKED && !MASK_AHEAD) {
                 dma_wait<2 * LDW>();   // this step's mask values (and tile t+2) landed
-                launder(mcur[0]);
-                launder(mcur[1]);
+                launder_mask(mcur[0]);
+                launder_mask(mcur[1]);
             }
             const uint32_t v_slot = (uint32_t)(t & (STAGES - 1)) * TILE_BYTES;
             const uint32_t k_slot = (uint32_t)((t + 1) & (STAGES - 1)) * TILE_BYTES;
@@ -540,8 +533,8 @@ fwd16_ring_kernel(const FwdParams p) {
         }
         dma_wait<2 * LDW>();   // everything but tile t+3 landed
         if constexpr (MASK_AHEAD) {
-            launder(mnext[0]);
-            launder(mnext[1]);
+            launder_mask(mnext[0]);
+            launder_mask(mnext[1]);
         }
         __syncthreads();
     };
@@ -576,7 +569,7 @@ fwd16_ring_kernel(const FwdParams p) {
         issue_tile(1);
         dma_wait<2 * LDW>();   // Q, tile 0 and the mask loads before it landed
         launder_q();
-        if constexpr (MASK_AHEAD) launder(mask_b[1]);
+        if constexpr (MASK_AHEAD) launder_mask(mask_b[1]);
         __syncthreads();
         // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
         step(int_c<1>{}, bool_c<false>{}, -1, mask_b, mask_a);
@@ -588,26 +581,31 @@ fwd16_ring_kernel(const FwdParams p) {
     }
     dma_wait<0>();   // the ring's trailing (empty) tile loads retire before the workgroup ends
 
-    const float l = half_swap_sum(l_run);
-    if (!row_valid) return;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    scalar* orow = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h + row * p.o_stride_i;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l = half_swap_sum(l_run[rb]);
+        if (!row_valid[rb]) continue;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        scalar* orow = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h + row[rb] * p.o_stride_i;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int d = 32 * db + 8 * a + 4 * hh;
-            f32x4 val;
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) val[c] = o[db][4 * a + c] * inv;
-            *(vec4*)(orow + d) = __builtin_convertvector(val, vec4);
+            for (int a = 0; a < 4; ++a) {
+                const int d = 32 * db + 8 * a + 4 * hh;
+                f32x4 val;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) val[c] = o[rb][db][4 * a + c] * inv;
+                *(vec4*)(orow + d) = __builtin_convertvector(val, vec4);
+            }
         }
     }
 }
 
 template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW>
 hipError_t launch_ring_one(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd16_ring_kernel<Tr, DP, MASKK, SOFTCAP, RAW>), dim3(grid), dim3(kRingThreads), 0, stream, p);
+    constexpr int RB = kRingRowBlocks;
+    hipLaunchKernelGGL((fwd16_ring_kernel<Tr, DP, MASKK, SOFTCAP, RAW, RB>), dim3(grid), dim3(ring_threads(RB)), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
