@@ -105,8 +105,10 @@ def cpu_baseline(prob, out_gpu: torch.Tensor, target_s: float):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU ramps its clocks over the first ~0.1-0.3 s of sustained load: the default warmup
+    # (about 0.35 s of the GQA causal workload) lets the timed steps see the steady state
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="gqa_causal", choices=list(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -7,6 +7,7 @@
 // rejected instead of silently reading plane 0, and an empty key range writes zeros.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -163,6 +164,21 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     return FA_OK;
 }
 
+// Compute units of the current device, queried once per device (no synchronisation).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,14 +211,24 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();  // a stale error from unrelated work must not be reported as ours
+    p.items_per_xcd = plan.grid / 8;
+    int grid = plan.grid;
+    if (plan.ring) {
+        // the ring kernel is persistent: one workgroup per CU (rounded down to whole XCDs)
+        // walks the work items; small problems keep one workgroup per item
+        const int cus = device_cu_count();
+        if (cus <= 0) return fail(FA_ERR_HIP, "cannot query the compute-unit count of the current device");
+        const int persist = cus / 8 * 8;
+        if (persist >= 8 && grid > persist) grid = persist;
+    }
     hipError_t err;
     if (dtype == FA_DTYPE_BF16)
-        err = plan.ring ? fa::launch_bf16_ring(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s)
-                        : fa::launch_bf16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
+        err = plan.ring ? fa::launch_bf16_ring(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s)
+                        : fa::launch_bf16(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s);
     else if (dtype == FA_DTYPE_F16)
-        err = plan.ring ? fa::launch_f16_ring(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s)
-                        : fa::launch_f16(p, plan.dp, plan.grid, plan.maskk, p.softcap > 0.0f, s);
-    else err = fa::launch_f32(p, plan.dp, plan.grid, plan.maskk != 0, p.softcap > 0.0f, s);
+        err = plan.ring ? fa::launch_f16_ring(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s)
+                        : fa::launch_f16(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s);
+    else err = fa::launch_f32(p, plan.dp, grid, plan.maskk != 0, p.softcap > 0.0f, s);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;
 }

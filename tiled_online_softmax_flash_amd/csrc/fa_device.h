@@ -175,18 +175,12 @@ __device__ __forceinline__ void dma_lds16(u32x4 rsrc, uint32_t lds_addr, uint32_
                  : "m0");
 }
 
-// Wait until at most N vector-memory loads of this wave are in flight (loads retire in order).
+// Wait until at most N vector-memory operations of this wave are in flight (loads retire in
+// order; stores count too).
 template <int N>
 __device__ __forceinline__ void dma_wait() {
-    static_assert(N >= 0 && N <= 15, "vmcnt range");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else static_assert(N == 0, "add the vmcnt value");
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Raw buffer descriptor as four wave-uniform dwords (gfx9 family, stride 0, byte-addressed).

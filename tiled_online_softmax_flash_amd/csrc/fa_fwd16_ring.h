@@ -93,34 +93,174 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int CPR = DP / 8;                  // 16-byte chunks per row
     constexpr int TILE_BYTES = BN * ROWB;
     constexpr int V_REGION = STAGES * TILE_BYTES;   // K slots [0, V_REGION), V slots after
-    constexpr int LDW = TILE_BYTES / 1024 / WAVES;  // 1 KiB DMA ops per wave per operand per tile
+    // K/V ring loads are issued by the last DMA_WAVES waves.  With two waves per SIMD those are
+    // the younger wave of each pair; they also run at raised issue priority (below).  Measured
+    // on the masked and KV-cache workloads this is 1-3 % faster than every wave loading a share
+    // at equal priority (the older wave of a pair otherwise tends to finish each ring step
+    // early and wait at the barrier).
+    constexpr int DMA_WAVES = RB == 1 ? WAVES / 2 : WAVES;
+    constexpr int DMA_FIRST = WAVES - DMA_WAVES;   // first loading wave
+    constexpr int LDW = TILE_BYTES / 1024 / DMA_WAVES;  // 1 KiB DMA ops per loading wave per operand per tile
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
+    constexpr int NSTORE = RB * (DP / 8);        // global store instructions of a wave's epilogue
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
     using MaskH = MaskHalf<MASKK>;
     static_assert(DP == 64 || DP == 128, "ring kernel covers head dims 64 and 128");
-    static_assert(LDW >= 1, "tile must cover every wave");
+    static_assert(LDW >= 1 && LDW * DMA_WAVES * 1024 == TILE_BYTES, "tile must split evenly over the loading waves");
     static_assert((STAGES - 1) * TILE_BYTES + HB * ROWB + 12 * ROWB + 8 < 65536,
                   "LDS operand offsets must fit the 16-bit immediate");
 
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGES * TILE_BYTES];
     const uint32_t lds_base = lds_addr(lds);
 
-    const WorkItem w = decode_work(p, blockIdx.x);
-    if (!w.valid) return;
-    const int b = w.b, h = w.h;
-    const int kvh = h / p.group;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lr = lane & 31;
     const int hh = lane >> 5;
     const int D = DP;
+    if (DMA_FIRST > 0 && wave >= DMA_FIRST) __builtin_amdgcn_s_setprio(1);   // the loading waves
+    const float kfac = p.kfac;
+    const float th_x = kRescaleLog2 / kfac;
+    const scalar* __restrict__ qg = (const scalar*)p.q;
 
-    const KeyRule rule = make_rule(p, b);
-    const int64_t q0 = (int64_t)w.qt * kRingBlockRows;
-    const int64_t q_last = (q0 + kRingBlockRows < p.sq ? q0 + kRingBlockRows : p.sq) - 1;
+    // ---- DMA source offsets: DMA op i of a tile writes physical 16-byte chunks [64 i, 64 i + 64)
+    // (K and V alike); a half-tile holds HB * CPR chunks.  With q the chunk index inside half H:
+    //   K chunk pc of half H: slice ks = q / 64, row r = (q / 2) % 32, position c = q % 2
+    //     (q = pc within the half) <- key 32 H + kk(r), dim chunk 2 ks + (c ^ bit 3 of r);
+    //   V chunk pc of half H: block db = q / 128, key j = (q / 4) % 32, chunk c = q % 4
+    //     <- key 32 H + j, dim chunk 4 db + c.
+    constexpr int HALF_CHUNKS = HB * CPR;
+    uint32_t k_src[LDW], v_src[LDW];
+#pragma unroll
+    for (int j = 0; j < LDW; ++j) {
+        const int pc = 64 * (((wave - DMA_FIRST) & (DMA_WAVES - 1)) * LDW + j) + lane;   // chunk index in the tile
+        const int hf = pc / HALF_CHUNKS;
+        const int q = pc % HALF_CHUNKS;
+        {
+            const int ks = q / 64, r = (q >> 1) & 31, c = q & 1;
+            const int key = 32 * hf + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);   // kk(r)
+            k_src[j] = (uint32_t)(key * ROWB + (2 * ks + (c ^ ((r >> 3) & 1))) * 16);
+        }
+        {
+            const int db = q / 128, key = 32 * hf + ((q >> 2) & 31), c = q & 3;
+            v_src[j] = (uint32_t)(key * ROWB + (4 * db + c) * 16);
+        }
+    }
+
+    // ---- LDS operand addresses: one per-lane base per operand; ring slot, half-tile, K slice and
+    // V block are immediates.
+    // K (A operand of S^T = K Q^T): lane (lr, hh) reads row lr, dims 16 ks + 8 hh .. +7.
+    const uint32_t k_base = (uint32_t)(lr * 32 + ((hh ^ ((lr >> 3) & 1)) << 4));
+    // V^T (A operand of O^T += V^T P^T) through ds_read_b64_tr_b16.  Source lane
+    // l = 16 g + 4 k + c points at key 16 hh + 8 j + 4 r + k and dims 32 db + 16 g + 4 c .. +3 of
+    // the half-tile (g = bit 4 of l, hh = bit 5); the transpose hands lane l dims d = l % 32 of
+    // those four keys.
+    const uint32_t v_base = (uint32_t)V_REGION + (uint32_t)((16 * hh + ((lane >> 2) & 3)) * 64 +
+                                                            ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
+
+    // ---- Work items (batch, query head, 256-row query tile).  The workgroup is persistent: the
+    // workgroup with id j runs on XCD j % 8 and takes, in round r, XCD-local slot
+    // r * ncu + (c or ncu - 1 - c) (c = j / 8, ncu = workgroups per XCD; the order within a
+    // round alternates so that the heavy-first slot order of decode_work pairs heavy items
+    // with light ones on each CU).  While an item runs its last two ring steps, the ring slots it
+    // no longer needs receive the next item's first two K/V tiles and the next item's Q is
+    // loaded, so the next item starts without a memory round trip (unmasked variants; masked
+    // ones keep their mask buffers busy to the end and start each item afresh).
+    const int xcd = blockIdx.x & 7;
+    const int cu = blockIdx.x >> 3;
+    const int ncu = (int)(gridDim.x >> 3);
+    auto slot_of_round = [&](int r) -> int { return r * ncu + ((r & 1) ? ncu - 1 - cu : cu); };
+    struct ItemGeo {
+        WorkItem w;
+        KeyRule rule;
+        int64_t q0, q_last;
+        int kt_begin, n_tiles;
+        const char* kg;
+        const char* vg;
+    };
+    auto item_geo = [&](int slot) __attribute__((always_inline)) -> ItemGeo {
+        ItemGeo g;
+        g.w = decode_work(p, slot * 8 + xcd);
+        g.w.valid = g.w.valid && slot < p.items_per_xcd;
+        if (!g.w.valid) g.w.b = g.w.h = g.w.qt = 0;   // never index past the inputs
+        g.rule = make_rule(p, g.w.b);
+        g.q0 = (int64_t)g.w.qt * kRingBlockRows;
+        g.q_last = (g.q0 + kRingBlockRows < p.sq ? g.q0 + kRingBlockRows : p.sq) - 1;
+        const int64_t lo_wg = g.rule.lo(g.q0), hi_wg = g.rule.hi(g.q_last);
+        g.kt_begin = hi_wg >= lo_wg ? (int)(lo_wg / BN) : 0;
+        g.n_tiles = hi_wg >= lo_wg ? (int)(hi_wg / BN) - g.kt_begin + 1 : 0;
+        const int kvh = g.w.h / p.group;
+        g.kg = (const char*)p.k + ((int64_t)g.w.b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
+        g.vg = (const char*)p.v + ((int64_t)g.w.b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
+        return g;
+    };
+    // Q fragment loads of one item into q: lane (m, hh) of row block rb holds
+    // Q[row][16*ks + 8*hh .. +7].  Through inline asm like the K/V ring, so that a ring wait
+    // retires them together with ring tiles and the tile loop holds no register the compiler
+    // sees as loaded from memory (its wait-count pass would otherwise drain the ring).
+    auto load_q = [&](const ItemGeo& g, vec8 (&q)[RB][NKS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int64_t r = g.q0 + wave * WROWS + 32 * rb + lr;
+            const scalar* qrow = qg + (((int64_t)g.w.b * p.heads + g.w.h) * p.sq + (r < p.sq ? r : 0)) * D;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4 t;
+                asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(t) : "v"(qrow + 16 * ks + 8 * hh));
+                q[rb][ks] = __builtin_bit_cast(vec8, t);
+            }
+        }
+    };
+    // Tile t of item g into ring slot `slot` (tiles past the item's end, or of an invalid item,
+    // are loaded through an empty descriptor: they write zeros).
+    auto issue_tile_of = [&](const ItemGeo& g, int t, int slot) __attribute__((always_inline)) {
+        const int64_t k0 = (int64_t)(g.kt_begin + t) * BN;
+        int64_t keys = g.rule.L - k0;
+        keys = keys < 0 ? 0 : (keys > BN ? BN : keys);
+        if (t >= g.n_tiles || !g.w.valid) keys = 0;
+        const int bytes = (int)(keys * ROWB);
+        const int64_t base_off = keys > 0 ? k0 * ROWB : 0;
+        const u32x4 rk = make_rsrc_words(g.kg + base_off, bytes);
+        const u32x4 rv = make_rsrc_words(g.vg + base_off, bytes);
+        const uint32_t so = (uint32_t)(slot & (STAGES - 1)) * TILE_BYTES;
+        const uint32_t sk = lds_base + so;
+        const uint32_t sv = lds_base + V_REGION + so;
+        if (wave >= DMA_FIRST) {
+#pragma unroll
+            for (int j = 0; j < LDW; ++j) {
+                const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane((wave - DMA_FIRST) * LDW + j);
+                dma_lds16(rk, sk + 1024u * op, k_src[j]);
+                dma_lds16(rv, sv + 1024u * op, v_src[j]);
+            }
+        }
+    };
+    // Wait until every ring load of this wave but the last tile's has landed (loads issued
+    // before that tile included); waves that issue no ring loads wait for everything.
+    auto ring_wait = [&]() __attribute__((always_inline)) {
+        if (wave >= DMA_FIRST) dma_wait<2 * LDW>();
+        else dma_wait<0>();
+    };
+
+    int ring_base = 0;     // ring position of the current item's tile 0 (slot = position % 4)
+    bool pre = false;      // the current item's Q and first two tiles are already in flight
+    // Q fragments of the current item.  With pre, the previous item's last ring step loaded them
+    // in place: that step's own Q.K products only score half-tiles past its item, which no later
+    // block reads, so they may read these registers while the loads are in flight.
+    vec8 qf[RB][NKS];
+    // O stores of the previous item still in flight (they count in vmcnt like loads): the
+    // first ring wait of an item that was prefetched lets exactly these stay outstanding
+    bool prev_stores = false;
+    ItemGeo cur = item_geo(slot_of_round(0));
+    for (int round = 0; cur.w.valid; ++round) {
+    const ItemGeo nxt = item_geo(slot_of_round(round + 1));
+    const WorkItem w = cur.w;
+    const int b = w.b, h = w.h;
+    const KeyRule rule = cur.rule;
+    const int64_t q0 = cur.q0;
+    const int64_t q_last = cur.q_last;
     const int64_t wr0 = q0 + wave * WROWS;
     const bool wave_has_rows = wr0 < p.sq;
     const int64_t wr1 = (wr0 + WROWS - 1 < p.sq ? wr0 + WROWS - 1 : p.sq - 1);
@@ -140,29 +280,10 @@ fwd16_ring_kernel(const FwdParams p) {
     const int64_t w_lo_min = rule.lo(wr0), w_lo_max = rule.lo(wr1);
     const int64_t w_hi_min = rule.hi(wr0), w_hi_max = rule.hi(wr1);
 
-    const int64_t lo_wg = rule.lo(q0), hi_wg = rule.hi(q_last);
-    const int kt_begin = hi_wg >= lo_wg ? (int)(lo_wg / BN) : 0;
-    const int n_tiles = hi_wg >= lo_wg ? (int)(hi_wg / BN) - kt_begin + 1 : 0;
+    const int kt_begin = cur.kt_begin;
+    const int n_tiles = cur.n_tiles;
 
-    const scalar* __restrict__ qg = (const scalar*)p.q;
-    const char* kg = (const char*)p.k + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
-    const char* vg = (const char*)p.v + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
-
-    // ---- Q fragments: lane (m, hh) holds Q[row][16*ks + 8*hh .. +7].  The loads go through
-    // inline asm like the K/V ring, so the first ring wait retires them together with the first
-    // tile (the two latencies overlap), and the tile loop holds no register the compiler sees as
-    // loaded from memory (its wait-count pass would otherwise drain the ring inside the loop).
-    vec8 qf[RB][NKS];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const scalar* qrow = qg + (((int64_t)b * p.heads + h) * p.sq + (row_valid[rb] ? row[rb] : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4 t;
-            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(t) : "v"(qrow + 16 * ks + 8 * hh));
-            qf[rb][ks] = __builtin_bit_cast(vec8, t);
-        }
-    }
+    if (!pre) load_q(cur, qf);
     auto launder_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -198,52 +319,19 @@ fwd16_ring_kernel(const FwdParams p) {
         m_run[rb] = neg_inf();
         l_run[rb] = 0.0f;
     }
-    const float kfac = p.kfac;
-    const float th_x = kRescaleLog2 / kfac;
 
-    // ---- DMA source offsets: DMA op i of a tile writes physical 16-byte chunks [64 i, 64 i + 64)
-    // (K and V alike); a half-tile holds HB * CPR chunks.  With q the chunk index inside half H:
-    //   K chunk pc of half H: slice ks = q / 64, row r = (q / 2) % 32, position c = q % 2
-    //     (q = pc within the half) <- key 32 H + kk(r), dim chunk 2 ks + (c ^ bit 3 of r);
-    //   V chunk pc of half H: block db = q / 128, key j = (q / 4) % 32, chunk c = q % 4
-    //     <- key 32 H + j, dim chunk 4 db + c.
-    constexpr int HALF_CHUNKS = HB * CPR;
-    uint32_t k_src[LDW], v_src[LDW];
-#pragma unroll
-    for (int j = 0; j < LDW; ++j) {
-        const int pc = 64 * (wave * LDW + j) + lane;   // physical chunk index in the tile
-        const int hf = pc / HALF_CHUNKS;
-        const int q = pc % HALF_CHUNKS;
-        {
-            const int ks = q / 64, r = (q >> 1) & 31, c = q & 1;
-            const int key = 32 * hf + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);   // kk(r)
-            k_src[j] = (uint32_t)(key * ROWB + (2 * ks + (c ^ ((r >> 3) & 1))) * 16);
-        }
-        {
-            const int db = q / 128, key = 32 * hf + ((q >> 2) & 31), c = q & 3;
-            v_src[j] = (uint32_t)(key * ROWB + (4 * db + c) * 16);
-        }
-    }
-
+    // The item's tile t sits at ring position ring_base + t.  A step issues ring position
+    // t + 3: the item's own tile while there is one, then (pre_next) the next item's tiles 0 and
+    // 1 at positions t_last + 2 and t_last + 3 of the last two steps, else an empty tile.
+    const int n_pairs = (n_tiles + 1) / 2;
+    const int t_last = 2 * n_pairs - 1;   // last ring step of the item (steps -1 .. t_last)
+    // (one row block per wave: the epilogue's store count that the next item's first wait
+    // allows for is then fixed)
+    const bool pre_next = RB == 1 && !MASKED && nxt.w.valid && nxt.n_tiles > 0 && n_tiles > 0;
     auto issue_tile = [&](int t) __attribute__((always_inline)) {
-        // tiles past the end are loaded through an empty descriptor: they write zeros
-        const int64_t k0 = (int64_t)(kt_begin + t) * BN;
-        int64_t keys = rule.L - k0;
-        keys = keys < 0 ? 0 : (keys > BN ? BN : keys);
-        if (t >= n_tiles) keys = 0;
-        const int bytes = (int)(keys * ROWB);
-        const int64_t base_off = keys > 0 ? k0 * ROWB : 0;
-        const u32x4 rk = make_rsrc_words(kg + base_off, bytes);
-        const u32x4 rv = make_rsrc_words(vg + base_off, bytes);
-        const uint32_t slot = (uint32_t)(t & (STAGES - 1)) * TILE_BYTES;
-        const uint32_t sk = lds_base + slot;
-        const uint32_t sv = lds_base + V_REGION + slot;
-#pragma unroll
-        for (int j = 0; j < LDW; ++j) {
-            const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane(wave * LDW + j);
-            dma_lds16(rk, sk + 1024u * op, k_src[j]);
-            dma_lds16(rv, sv + 1024u * op, v_src[j]);
-        }
+        if (pre_next && t == t_last + 2) issue_tile_of(nxt, 0, ring_base + t);
+        else if (pre_next && t == t_last + 3) issue_tile_of(nxt, 1, ring_base + t);
+        else issue_tile_of(cur, t, ring_base + t);
     };
 
     const int key_base = kt_begin * BN;
@@ -310,16 +398,6 @@ fwd16_ring_kernel(const FwdParams p) {
     // full(u) implies that the wave attends half-tile u: [fa, fb] lies inside [ua, ub]
     auto full = [&](int u) __attribute__((always_inline)) { return u >= fa && u <= fb; };
 
-    // ---- LDS operand addresses: one per-lane base per operand; ring slot, half-tile, K slice and
-    // V block are immediates.
-    // K (A operand of S^T = K Q^T): lane (lr, hh) reads row lr, dims 16 ks + 8 hh .. +7.
-    const uint32_t k_base = (uint32_t)(lr * 32 + ((hh ^ ((lr >> 3) & 1)) << 4));
-    // V^T (A operand of O^T += V^T P^T) through ds_read_b64_tr_b16.  Source lane
-    // l = 16 g + 4 k + c points at key 16 hh + 8 j + 4 r + k and dims 32 db + 16 g + 4 c .. +3 of
-    // the half-tile (g = bit 4 of l, hh = bit 5); the transpose hands lane l dims d = l % 32 of
-    // those four keys.
-    const uint32_t v_base = (uint32_t)V_REGION + (uint32_t)((16 * hh + ((lane >> 2) & 3)) * 64 +
-                                                            ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
     // score epilogue of one element: tracked units x (see RAW / SOFTCAP / MASKED)
     auto epi = [&](float sv, float mvv) __attribute__((always_inline)) -> float {
         if constexpr (SOFTCAP) {
@@ -514,6 +592,7 @@ fwd16_ring_kernel(const FwdParams p) {
                 load_mask_half(2 * t + 2, mcur[1]);
             }
         }
+        if (pre_next && t == t_last) load_q(nxt, qf);
         issue_tile(t + 3);
         if constexpr (KIND == 0) {
 #pragma unroll
@@ -521,17 +600,24 @@ fwd16_ring_kernel(const FwdParams p) {
                 p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = vec8((scalar)0.0f);
         } else {
             if constexpr (MASKED && !MASK_AHEAD) {
-                dma_wait<2 * LDW>();   // this step's mask values (and tile t+2) landed
+                ring_wait();   // this step's mask values (and tile t+2) landed
                 launder_mask(mcur[0]);
                 launder_mask(mcur[1]);
             }
-            const uint32_t v_slot = (uint32_t)(t & (STAGES - 1)) * TILE_BYTES;
-            const uint32_t k_slot = (uint32_t)((t + 1) & (STAGES - 1)) * TILE_BYTES;
+            const uint32_t v_slot = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
+            const uint32_t k_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
             using F = bool_c<KIND == 2>;
             xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0]);
             xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1]);
         }
-        dma_wait<2 * LDW>();   // everything but tile t+3 landed
+        if (pre && t == -1 && prev_stores) {
+            // everything but tile t+3 and the previous item's O stores (issued after this
+            // item's tile t+2 = 1) landed
+            if (wave >= DMA_FIRST) dma_wait<2 * LDW + NSTORE>();
+            else dma_wait<NSTORE>();
+        } else {
+            ring_wait();   // everything but tile t+3 landed
+        }
         if constexpr (MASK_AHEAD) {
             launder_mask(mnext[0]);
             launder_mask(mnext[1]);
@@ -565,12 +651,15 @@ fwd16_ring_kernel(const FwdParams p) {
             f1 = __builtin_amdgcn_readfirstlane(f1);
         }
         if constexpr (MASK_AHEAD) load_mask_half(0, mask_b[1]);
-        issue_tile(0);
-        issue_tile(1);
-        dma_wait<2 * LDW>();   // Q, tile 0 and the mask loads before it landed
+        if (!pre) {
+            issue_tile(0);
+            issue_tile(1);
+            ring_wait();   // Q, tile 0 and the mask loads before it landed
+        }
+        // (prefetched: the previous item's closing wait and barrier retired Q and tile 0)
         launder_q();
         if constexpr (MASK_AHEAD) launder_mask(mask_b[1]);
-        __syncthreads();
+        if (!pre) __syncthreads();
         // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
         step(int_c<1>{}, bool_c<false>{}, -1, mask_b, mask_a);
         run_pairs(int_c<0>{}, 0, a0);
@@ -579,27 +668,40 @@ fwd16_ring_kernel(const FwdParams p) {
         run_pairs(int_c<1>{}, f1, a1);
         run_pairs(int_c<0>{}, a1, n_pairs);
     }
-    dma_wait<0>();   // the ring's trailing (empty) tile loads retire before the workgroup ends
+    if (!pre_next) dma_wait<0>();   // nothing of this item's ring stays in flight
 
+    // A wave with any valid row issues all NSTORE stores (invalid lanes masked off); a wave
+    // without one issues none.
+    if (wave_has_rows) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float l = half_swap_sum(l_run[rb]);
-        if (!row_valid[rb]) continue;
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        scalar* orow = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h + row[rb] * p.o_stride_i;
+        for (int rb = 0; rb < RB; ++rb) {
+            const float l = half_swap_sum(l_run[rb]);
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            const bool ok = row_valid[rb];
+            scalar* orow = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h +
+                           (ok ? row[rb] : 0) * p.o_stride_i;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int d = 32 * db + 8 * a + 4 * hh;
-                f32x4 val;
+                for (int a = 0; a < 4; ++a) {
+                    const int d = 32 * db + 8 * a + 4 * hh;
+                    f32x4 val;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) val[c] = o[rb][db][4 * a + c] * inv;
-                *(vec4*)(orow + d) = __builtin_convertvector(val, vec4);
+                    for (int c = 0; c < 4; ++c) val[c] = o[rb][db][4 * a + c] * inv;
+                    const vec4 pk = __builtin_convertvector(val, vec4);
+                    if (ok) *(vec4*)(orow + d) = pk;
+                }
             }
         }
     }
+    prev_stores = wave_has_rows;
+    ring_base = pre_next ? ring_base + t_last + 2 : 0;
+    pre = pre_next;
+    cur = nxt;
+    }   // items
+    dma_wait<0>();   // no ring load stays in flight past the workgroup's end
 }
+
 
 template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW>
 hipError_t launch_ring_one(const FwdParams& p, int grid, hipStream_t stream) {

@@ -27,6 +27,7 @@ struct FwdParams {
     int q_tiles;                 // ceil(sq / kBlockRows)
     int pairs;                   // batch * q_tiles: (batch, query tile) pairs
     int xcd_groups;              // 1: group-major workgroup order (see decode_work)
+    int items_per_xcd;           // work items per XCD (the non-persistent grid / 8)
     int vec_kv;                  // q/k/v rows move in 16-byte pieces (dim and pointers allow it)
     int vec_mask;                // mask rows move in 16-byte pieces
     int vec_out;                 // output rows move in 4-element pieces
