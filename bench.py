@@ -33,7 +33,8 @@ from tiled_online_softmax_flash_amd.metrics import attended_counts, problem_work
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk_eff·D) + % of MI355X MFMA peak"
-KERNEL_SOURCES = ["fa_device.h", "fa_params.h", "fa_fwd16.h", "fa_fwd32.h"]
+KERNEL_SOURCES = ["fa_device.h", "fa_params.h", "fa_fwd16.h", "fa_fwd16_ring.h",
+                  "fa_fwd16_ring_consts.h", "fa_fwd32.h", "fa_launch.h", "fa_api.hip"]
 
 
 def kernel_hash() -> str:

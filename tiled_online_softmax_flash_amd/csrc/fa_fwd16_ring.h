@@ -104,6 +104,7 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NSTORE = RB * (DP / 8);        // global store instructions of a wave's epilogue
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
+    constexpr int NPRE = 4 * NDB < 12 ? 4 * NDB : 12;   // V reads a block issues for the next one
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
     using MaskH = MaskHalf<MASKK>;
@@ -467,6 +468,16 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     };
 
+    // Read r of the V^T operand reads of a block whose V half-tile starts OFFH bytes into the
+    // V tile in ring slot `slot`: half r % 2 of V^T fragment r / 2 (fragment f covers dims
+    // 32 (f % NDB) .. +31 and keys 16 (f / NDB) .. +15 of the half-tile).
+    auto read_vt = [&](auto offh_c, auto r_c, uint32_t slot) __attribute__((always_inline)) -> u32x2 {
+        constexpr int r = decltype(r_c)::value;
+        constexpr int f = r / 2, hv = r % 2, j = f / NDB, db = f % NDB;
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(lds + slot + v_base + (decltype(offh_c)::value + db * 2048 + (8 * j + 4 * hv) * 64))));
+    };
+
     // ---- Pipelined block u: O^T += V^T P^T for half-tile u-1, the softmax of half-tile u
     // (scores s_cur, probabilities into p_cur) and S^T = K Q^T for half-tile u+1 (into s_nxt),
     // for each of the wave's RB row blocks; every K/V operand fragment read from LDS feeds the RB
@@ -482,29 +493,45 @@ fwd16_ring_kernel(const FwdParams p) {
     // WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
     auto xbody = [&](auto full_c, auto with_pv_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
                      f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], vec8 (&p_prev)[RB][2], vec8 (&p_cur)[RB][2],
-                     const MaskH (&mh)[RB]) __attribute__((always_inline)) {
+                     const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE]) __attribute__((always_inline)) {
         constexpr bool WITH_PV = decltype(with_pv_c)::value;
+        constexpr int PAR = decltype(par_c)::value;
         constexpr int NPV = WITH_PV ? 2 * NDB : 0;   // V^T fragments (one per P.V MFMA per row block)
         constexpr int NF = NPV + NKS;                // operand fragments of the block
         constexpr int NM = RB * NF;                  // MFMAs of the block
         // LDS operand reads, in the order the MFMAs consume them: read r < 2*NPV is half r % 2
         // of V^T fragment r / 2 (4 keys x 4 dims per transpose read), read 2*NPV + ks is K
         // fragment ks.  Reads run AHEAD operands in front of the first MFMA that needs them
-        // (the compiler's waits then let each MFMA wait for its own reads only).
+        // (the compiler's waits then let each MFMA wait for its own reads only).  The first
+        // NPRE reads of a block with P.V products come from the block before it (rpre): they
+        // read V, which is resident one block earlier, so a block starts without an LDS round
+        // trip.  Reads NR .. NR + NPRE - 1 of this block are those of the next block: V of the
+        // same tile's other half (PAR 0), or the first half of the next step's V tile, which
+        // sits in this step's K slot (PAR 1).  A first block without P.V (PAR 0) is followed by
+        // another one and issues none.
         constexpr int NR = 2 * NPV + NKS;
         constexpr int AHEAD = 12;
-        constexpr int OFFH = decltype(par_c)::value * HB * ROWB;
+        constexpr int OFFH = PAR * HB * ROWB;
+        constexpr int PRE_IN = WITH_PV ? NPRE : 0;
+        constexpr int PRE_OUT = (WITH_PV || PAR == 1) ? NPRE : 0;
+        constexpr int NT = NR + PRE_OUT;
+        static_assert(PRE_IN == 0 || AHEAD <= NR,
+                      "a next-block read may only reuse a leading read's entry from the unit that consumes it on");
         u32x2 rv[NPV > 0 ? 2 * NPV : 1];
         u32x4 rk[NKS];
         auto issue = [&](auto r_c) __attribute__((always_inline)) {
             constexpr int r = decltype(r_c)::value;
-            if constexpr (r < 2 * NPV) {
-                constexpr int f = r / 2, hv = r % 2, j = f / NDB, db = f % NDB;
-                rv[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(lds + v_slot + v_base + (OFFH + db * 2048 + (8 * j + 4 * hv) * 64))));
-            } else {
+            if constexpr (r < PRE_IN) {
+                // issued by the block before
+            } else if constexpr (r < 2 * NPV) {
+                rv[r] = read_vt(int_c<OFFH>{}, r_c, v_slot);
+            } else if constexpr (r < NR) {
                 constexpr int ks = r - 2 * NPV;
                 rk[ks] = *(const u32x4*)(lds + k_slot + k_base + (OFFH + ks * 1024));
+            } else {
+                constexpr int rn = r - NR;
+                if constexpr (PAR == 0) rpre[rn] = read_vt(int_c<HB * ROWB>{}, int_c<rn>{}, v_slot);
+                else rpre[rn] = read_vt(int_c<0>{}, int_c<rn>{}, k_slot);
             }
         };
         static_for<0, (NR < AHEAD ? NR : AHEAD)>(issue);
@@ -517,11 +544,23 @@ fwd16_ring_kernel(const FwdParams p) {
                 constexpr int last = f < NPV ? 2 * f + 1 : NPV + f;   // last read fragment f needs
                 constexpr int prev = f == 0 ? -1 : (f - 1 < NPV ? 2 * (f - 1) + 1 : NPV + f - 1);
                 constexpr int top = NR < AHEAD ? NR : AHEAD;
-                constexpr int from = f == 0 ? top : (prev + 1 + AHEAD < NR ? prev + 1 + AHEAD : NR);
-                constexpr int upto = last + 1 + AHEAD < NR ? last + 1 + AHEAD : NR;
+                constexpr int from = f == 0 ? top : (prev + 1 + AHEAD < NT ? prev + 1 + AHEAD : NT);
+                constexpr int upto = last + 1 + AHEAD < NT ? last + 1 + AHEAD : NT;
+                // the fragment is taken before this unit's reads are issued: with head dim 64 they
+                // already include the next block's leading reads, which reuse the rpre entries
+                // this unit consumes
+                if constexpr (f < NPV) {
+                    auto vt = [&](auto i_c) __attribute__((always_inline)) -> u32x2 {
+                        constexpr int i = decltype(i_c)::value;
+                        if constexpr (i < PRE_IN) return rpre[i];
+                        else return rv[i];
+                    };
+                    const u32x2 lo = vt(int_c<2 * f>{}), hi = vt(int_c<2 * f + 1>{});
+                    frag = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    frag = rk[f - NPV];
+                }
                 static_for<(from < upto ? from : upto), upto>(issue);
-                if constexpr (f < NPV) frag = u32x4{rv[2 * f][0], rv[2 * f][1], rv[2 * f + 1][0], rv[2 * f + 1][1]};
-                else frag = rk[f - NPV];
             }
             if constexpr (f < NPV) {
                 constexpr int j = f / NDB, db = f % NDB;
@@ -575,6 +614,9 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr bool MASK_AHEAD = MASKED && DP == 64;
     f32x16 s_even[RB], s_odd[RB];
     vec8 p_even[RB][2], p_odd[RB][2];
+    u32x2 rpre[NPRE];   // leading V operand reads of the next block, issued by the block before
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) rpre[i] = u32x2{0u, 0u};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         s_even[rb] = s_odd[rb] = f32x16(0.0f);
@@ -598,6 +640,11 @@ fwd16_ring_kernel(const FwdParams p) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = vec8((scalar)0.0f);
+            // the next step's first block expects its leading V reads in flight
+            const uint32_t vn_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
+            static_for<0, NPRE>([&](auto r_c) __attribute__((always_inline)) {
+                rpre[decltype(r_c)::value] = read_vt(int_c<0>{}, r_c, vn_slot);
+            });
         } else {
             if constexpr (MASKED && !MASK_AHEAD) {
                 ring_wait();   // this step's mask values (and tile t+2) landed
@@ -607,8 +654,8 @@ fwd16_ring_kernel(const FwdParams p) {
             const uint32_t v_slot = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
             const uint32_t k_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
             using F = bool_c<KIND == 2>;
-            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0]);
-            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1]);
+            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre);
+            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre);
         }
         if (pre && t == -1 && prev_stores) {
             // everything but tile t+3 and the previous item's O stores (issued after this
