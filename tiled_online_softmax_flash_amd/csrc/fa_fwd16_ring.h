@@ -93,13 +93,11 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int CPR = DP / 8;                  // 16-byte chunks per row
     constexpr int TILE_BYTES = BN * ROWB;
     constexpr int V_REGION = STAGES * TILE_BYTES;   // K slots [0, V_REGION), V slots after
-    // K/V ring loads are issued by the last DMA_WAVES waves.  With two waves per SIMD those are
-    // the younger wave of each pair; they also run at raised issue priority (below).  Measured
-    // on the masked and KV-cache workloads this is 1-3 % faster than every wave loading a share
-    // at equal priority (the older wave of a pair otherwise tends to finish each ring step
-    // early and wait at the barrier).
-    constexpr int DMA_WAVES = RB == 1 ? WAVES / 2 : WAVES;
-    constexpr int DMA_FIRST = WAVES - DMA_WAVES;   // first loading wave
+    // Every wave issues an equal share of the K/V ring loads, one load at a time between the
+    // MFMAs of a step's first block: a burst of loads at the start of a step would hold up the
+    // issuing wave's MFMA stream (and the whole workgroup at the step's barrier) while the
+    // loads are accepted.
+    constexpr int DMA_WAVES = WAVES;
     constexpr int LDW = TILE_BYTES / 1024 / DMA_WAVES;  // 1 KiB DMA ops per loading wave per operand per tile
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NSTORE = RB * (DP / 8);        // global store instructions of a wave's epilogue
@@ -122,7 +120,6 @@ fwd16_ring_kernel(const FwdParams p) {
     const int lr = lane & 31;
     const int hh = lane >> 5;
     const int D = DP;
-    if (DMA_FIRST > 0 && wave >= DMA_FIRST) __builtin_amdgcn_s_setprio(1);   // the loading waves
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
     const scalar* __restrict__ qg = (const scalar*)p.q;
@@ -137,7 +134,7 @@ fwd16_ring_kernel(const FwdParams p) {
     uint32_t k_src[LDW], v_src[LDW];
 #pragma unroll
     for (int j = 0; j < LDW; ++j) {
-        const int pc = 64 * (((wave - DMA_FIRST) & (DMA_WAVES - 1)) * LDW + j) + lane;   // chunk index in the tile
+        const int pc = 64 * (wave * LDW + j) + lane;   // chunk index in the tile
         const int hf = pc / HALF_CHUNKS;
         const int q = pc % HALF_CHUNKS;
         {
@@ -215,35 +212,42 @@ fwd16_ring_kernel(const FwdParams p) {
             }
         }
     };
-    // Tile t of item g into ring slot `slot` (tiles past the item's end, or of an invalid item,
-    // are loaded through an empty descriptor: they write zeros).
-    auto issue_tile_of = [&](const ItemGeo& g, int t, int slot) __attribute__((always_inline)) {
+    // Loads of tile t of item g into ring slot `slot` (tiles past the item's end, or of an
+    // invalid item, are loaded through an empty descriptor: they write zeros).  A plan is worked
+    // out on the scalar unit; its NDMA loads per wave are then issued one by one.
+    struct DmaPlan {
+        u32x4 rk, rv;
+        uint32_t sk, sv;
+    };
+    constexpr int NDMA = 2 * LDW;   // ring loads per wave per tile: K and V alternately
+    auto plan_tile_of = [&](const ItemGeo& g, int t, int slot) __attribute__((always_inline)) -> DmaPlan {
         const int64_t k0 = (int64_t)(g.kt_begin + t) * BN;
         int64_t keys = g.rule.L - k0;
         keys = keys < 0 ? 0 : (keys > BN ? BN : keys);
         if (t >= g.n_tiles || !g.w.valid) keys = 0;
         const int bytes = (int)(keys * ROWB);
         const int64_t base_off = keys > 0 ? k0 * ROWB : 0;
-        const u32x4 rk = make_rsrc_words(g.kg + base_off, bytes);
-        const u32x4 rv = make_rsrc_words(g.vg + base_off, bytes);
+        DmaPlan d;
+        d.rk = make_rsrc_words(g.kg + base_off, bytes);
+        d.rv = make_rsrc_words(g.vg + base_off, bytes);
         const uint32_t so = (uint32_t)(slot & (STAGES - 1)) * TILE_BYTES;
-        const uint32_t sk = lds_base + so;
-        const uint32_t sv = lds_base + V_REGION + so;
-        if (wave >= DMA_FIRST) {
-#pragma unroll
-            for (int j = 0; j < LDW; ++j) {
-                const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane((wave - DMA_FIRST) * LDW + j);
-                dma_lds16(rk, sk + 1024u * op, k_src[j]);
-                dma_lds16(rv, sv + 1024u * op, v_src[j]);
-            }
-        }
+        d.sk = lds_base + so;
+        d.sv = lds_base + V_REGION + so;
+        return d;
+    };
+    // load i of this wave's share of a planned tile (1 KiB of K for even i, of V for odd i)
+    auto dma_issue = [&](const DmaPlan& d, auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value, j = i / 2;
+        const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane(wave * LDW + j);
+        if constexpr (i % 2 == 0) dma_lds16(d.rk, d.sk + 1024u * op, k_src[j]);
+        else dma_lds16(d.rv, d.sv + 1024u * op, v_src[j]);
+    };
+    auto dma_issue_all = [&](const DmaPlan& d) __attribute__((always_inline)) {
+        static_for<0, NDMA>([&](auto i_c) __attribute__((always_inline)) { dma_issue(d, i_c); });
     };
     // Wait until every ring load of this wave but the last tile's has landed (loads issued
-    // before that tile included); waves that issue no ring loads wait for everything.
-    auto ring_wait = [&]() __attribute__((always_inline)) {
-        if (wave >= DMA_FIRST) dma_wait<2 * LDW>();
-        else dma_wait<0>();
-    };
+    // before that tile included).
+    auto ring_wait = [&]() __attribute__((always_inline)) { dma_wait<NDMA>(); };
 
     int ring_base = 0;     // ring position of the current item's tile 0 (slot = position % 4)
     bool pre = false;      // the current item's Q and first two tiles are already in flight
@@ -324,15 +328,17 @@ fwd16_ring_kernel(const FwdParams p) {
     // The item's tile t sits at ring position ring_base + t.  A step issues ring position
     // t + 3: the item's own tile while there is one, then (pre_next) the next item's tiles 0 and
     // 1 at positions t_last + 2 and t_last + 3 of the last two steps, else an empty tile.
-    const int n_pairs = (n_tiles + 1) / 2;
-    const int t_last = 2 * n_pairs - 1;   // last ring step of the item (steps -1 .. t_last)
+    // steps 0 .. n_steps - 1 follow step -1; masked variants run steps in pairs (their mask
+    // buffers alternate), so their step count is even
+    const int n_steps = MASKED ? 2 * ((n_tiles + 1) / 2) : n_tiles;
+    const int t_last = n_steps - 1;   // last ring step of the item (steps -1 .. t_last)
     // (one row block per wave: the epilogue's store count that the next item's first wait
     // allows for is then fixed)
     const bool pre_next = RB == 1 && !MASKED && nxt.w.valid && nxt.n_tiles > 0 && n_tiles > 0;
-    auto issue_tile = [&](int t) __attribute__((always_inline)) {
-        if (pre_next && t == t_last + 2) issue_tile_of(nxt, 0, ring_base + t);
-        else if (pre_next && t == t_last + 3) issue_tile_of(nxt, 1, ring_base + t);
-        else issue_tile_of(cur, t, ring_base + t);
+    auto plan_tile = [&](int t) __attribute__((always_inline)) -> DmaPlan {
+        if (pre_next && t == t_last + 2) return plan_tile_of(nxt, 0, ring_base + t);
+        if (pre_next && t == t_last + 3) return plan_tile_of(nxt, 1, ring_base + t);
+        return plan_tile_of(cur, t, ring_base + t);
     };
 
     const int key_base = kt_begin * BN;
@@ -419,6 +425,7 @@ fwd16_ring_kernel(const FwdParams p) {
     //   each; 7: 16-bit packing and the denominator.  FULL: the half-tile needs no structural mask.
     struct SoftmaxState {
         float mt, alpha, m_safe, nmk, lsum;
+        uint32_t keep;
         bool moved;
     };
     auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, vec8 (&pf)[2],
@@ -426,15 +433,27 @@ fwd16_ring_kernel(const FwdParams p) {
         constexpr bool FULL = decltype(full_c)::value;
         constexpr int rb = decltype(rb_c)::value;
         if (ph == 0 || ph == 1) {
-            const int base = half_k0(u) + 16 * hh;
-            const int lo_rel = my_lo32[rb] - base;
-            const int hi_rel = my_hi32[rb] - base;
-            if (ph == 0) st.mt = neg_inf();
+            if (ph == 0) {
+                st.mt = neg_inf();
+                if constexpr (!FULL) {
+                    // bit v of keep: element v (key base + v) lies in the row's key range
+                    const int base = half_k0(u) + 16 * hh;
+                    const int lo_rel = my_lo32[rb] - base;
+                    const int hi_rel = my_hi32[rb] - base;
+                    const uint32_t below_hi = hi_rel < 0 ? 0u : (hi_rel >= 15 ? 0xffffu : (2u << hi_rel) - 1u);
+                    const uint32_t below_lo = lo_rel <= 0 ? 0u : (lo_rel >= 16 ? 0xffffu : (1u << lo_rel) - 1u);
+                    st.keep = below_hi & ~below_lo;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int v = 8 * ph + e;
                 float x = epi(sc[v], mask_val(mh, v));
-                if constexpr (!FULL) x = (v >= lo_rel && v <= hi_rel) ? x : neg_inf();
+                if constexpr (!FULL) {
+                    // all ones where element v is kept, else zero; masked elements become -inf
+                    const uint32_t sel = (uint32_t)((int32_t)(st.keep << (31 - v)) >> 31);
+                    x = __uint_as_float((sel & __float_as_uint(x)) | (~sel & 0xff800000u));
+                }
                 sc[v] = x;
                 st.mt = __builtin_fmaxf(st.mt, x);
             }
@@ -493,7 +512,7 @@ fwd16_ring_kernel(const FwdParams p) {
     // WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
     auto xbody = [&](auto full_c, auto with_pv_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
                      f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], vec8 (&p_prev)[RB][2], vec8 (&p_cur)[RB][2],
-                     const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE]) __attribute__((always_inline)) {
+                     const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE], auto&& unit_hook) __attribute__((always_inline)) {
         constexpr bool WITH_PV = decltype(with_pv_c)::value;
         constexpr int PAR = decltype(par_c)::value;
         constexpr int NPV = WITH_PV ? 2 * NDB : 0;   // V^T fragments (one per P.V MFMA per row block)
@@ -575,6 +594,7 @@ fwd16_ring_kernel(const FwdParams p) {
                 constexpr int srb = q % RB;
                 softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb]);
             });
+            unit_hook(m_c);
             // units (reads, wait, MFMA, softmax phases) stay in this order: a later unit's wait
             // must not run ahead of this unit's MFMA
             __builtin_amdgcn_sched_barrier(0);
@@ -635,8 +655,9 @@ fwd16_ring_kernel(const FwdParams p) {
             }
         }
         if (pre_next && t == t_last) load_q(nxt, qf);
-        issue_tile(t + 3);
+        const DmaPlan dp = plan_tile(t + 3);
         if constexpr (KIND == 0) {
+            dma_issue_all(dp);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = vec8((scalar)0.0f);
@@ -647,21 +668,31 @@ fwd16_ring_kernel(const FwdParams p) {
             });
         } else {
             if constexpr (MASKED && !MASK_AHEAD) {
-                ring_wait();   // this step's mask values (and tile t+2) landed
+                dma_wait<0>();   // this step's mask values (and tile t+2) landed
                 launder_mask(mcur[0]);
                 launder_mask(mcur[1]);
             }
             const uint32_t v_slot = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
             const uint32_t k_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
             using F = bool_c<KIND == 2>;
-            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre);
-            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre);
+            // tile t+3's loads, spread evenly over the first block's MFMAs
+            auto spread = [&](auto m_c) __attribute__((always_inline)) {
+                constexpr int m = decltype(m_c)::value;
+                constexpr int NMB = RB * ((decltype(with_pv_c)::value ? 2 * NDB : 0) + NKS);
+                static_assert(NMB >= NDMA, "one load per MFMA at most");
+                static_for<0, NDMA>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    if constexpr ((2 * i + 1) * NMB / (2 * NDMA) == m) dma_issue(dp, i_c);   // load i after MFMA m
+                });
+            };
+            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, spread);
+            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
+                  [](auto) {});
         }
         if (pre && t == -1 && prev_stores) {
             // everything but tile t+3 and the previous item's O stores (issued after this
             // item's tile t+2 = 1) landed
-            if (wave >= DMA_FIRST) dma_wait<2 * LDW + NSTORE>();
-            else dma_wait<NSTORE>();
+            dma_wait<NDMA + NSTORE>();
         } else {
             ring_wait();   // everything but tile t+3 landed
         }
@@ -678,11 +709,30 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     };
 
+    auto run_steps = [&](auto kind_c, int t0, int t1) __attribute__((always_inline)) {
+        for (int t = t0; t < t1; ++t) step(kind_c, bool_c<true>{}, t, mask_a, mask_b);
+    };
+
     if (n_tiles > 0) {
         // pair p holds blocks 4p+1 .. 4p+4, which touch half-tiles 4p .. 4p+5
-        const int n_pairs = (n_tiles + 1) / 2;
+        const int n_pairs = n_steps / 2;
         int a0, a1, f0, f1;
-        {
+        if constexpr (!MASKED) {
+            // step t runs blocks 2t+1 and 2t+2, which touch half-tiles 2t .. 2t+3; without mask
+            // buffers the kinds change from step to step
+            auto fdiv2 = [](int64_t x) -> int64_t { return x >> 1; };
+            auto cdiv2 = [](int64_t x) -> int64_t { return -((-x) >> 1); };
+            auto clip = [&](int64_t x, int64_t lo, int64_t hi) -> int { return (int)(x < lo ? lo : (x > hi ? hi : x)); };
+            // not skip: 2t+3 >= ua and 2t <= ub; full: 2t+1 >= fa and 2t+2 <= fb
+            a0 = clip(cdiv2((int64_t)ua - 3), 0, n_steps);
+            a1 = clip(fdiv2((int64_t)ub) + 1, a0, n_steps);
+            f0 = clip(cdiv2((int64_t)fa - 1), a0, a1);
+            f1 = clip(fdiv2((int64_t)fb - 2) + 1, f0, a1);
+            a0 = __builtin_amdgcn_readfirstlane(a0);
+            a1 = __builtin_amdgcn_readfirstlane(a1);
+            f0 = __builtin_amdgcn_readfirstlane(f0);
+            f1 = __builtin_amdgcn_readfirstlane(f1);
+        } else {
             auto fdiv4 = [](int64_t x) -> int64_t { return x >> 2; };
             auto cdiv4 = [](int64_t x) -> int64_t { return -((-x) >> 2); };
             auto clip = [&](int64_t x, int64_t lo, int64_t hi) -> int { return (int)(x < lo ? lo : (x > hi ? hi : x)); };
@@ -699,8 +749,8 @@ fwd16_ring_kernel(const FwdParams p) {
         }
         if constexpr (MASK_AHEAD) load_mask_half(0, mask_b[1]);
         if (!pre) {
-            issue_tile(0);
-            issue_tile(1);
+            dma_issue_all(plan_tile(0));
+            dma_issue_all(plan_tile(1));
             ring_wait();   // Q, tile 0 and the mask loads before it landed
         }
         // (prefetched: the previous item's closing wait and barrier retired Q and tile 0)
@@ -709,11 +759,19 @@ fwd16_ring_kernel(const FwdParams p) {
         if (!pre) __syncthreads();
         // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
         step(int_c<1>{}, bool_c<false>{}, -1, mask_b, mask_a);
-        run_pairs(int_c<0>{}, 0, a0);
-        run_pairs(int_c<1>{}, a0, f0);
-        run_pairs(int_c<2>{}, f0, f1);
-        run_pairs(int_c<1>{}, f1, a1);
-        run_pairs(int_c<0>{}, a1, n_pairs);
+        if constexpr (!MASKED) {
+            run_steps(int_c<0>{}, 0, a0);
+            run_steps(int_c<1>{}, a0, f0);
+            run_steps(int_c<2>{}, f0, f1);
+            run_steps(int_c<1>{}, f1, a1);
+            run_steps(int_c<0>{}, a1, n_steps);
+        } else {
+            run_pairs(int_c<0>{}, 0, a0);
+            run_pairs(int_c<1>{}, a0, f0);
+            run_pairs(int_c<2>{}, f0, f1);
+            run_pairs(int_c<1>{}, f1, a1);
+            run_pairs(int_c<0>{}, a1, n_pairs);
+        }
     }
     if (!pre_next) dma_wait<0>();   // nothing of this item's ring stays in flight
 
