@@ -104,9 +104,10 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     // (a mask must have 16-byte aligned rows there: sk a multiple of 4 and an aligned base)
     const int maskk = mask_planes == 0 ? 0 : (mask_dtype == FA_DTYPE_F32 ? 1 : 2);
     const bool mask_vec = mask_planes > 0 && sk % 4 == 0 && aligned(mask, maskk == 1 ? 16 : 8);
+    // (its K/V loads address one (batch, KV head) cache through 32-bit byte offsets)
     plan->ring = dtype != FA_DTYPE_F32 && (dim == 64 || dim == 128) && aligned(q, 16) &&
                  aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16))) &&
-                 (mask_planes == 0 || mask_vec);
+                 (mask_planes == 0 || mask_vec) && (int64_t)kv_capacity * dim * 2 < 0x7fffffffLL;
     const int block_rows = plan->ring ? fa::kRingBlockRows : fa::kBlockRows;
     if (mask_planes > 0 && (int64_t)block_rows * sk * 4 >= 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "sk %d is too long for a masked launch (a workgroup's mask rows "

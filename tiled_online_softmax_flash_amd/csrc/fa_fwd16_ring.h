@@ -212,35 +212,38 @@ fwd16_ring_kernel(const FwdParams p) {
             }
         }
     };
-    // Loads of tile t of item g into ring slot `slot` (tiles past the item's end, or of an
-    // invalid item, are loaded through an empty descriptor: they write zeros).  A plan is worked
-    // out on the scalar unit; its NDMA loads per wave are then issued one by one.
-    struct DmaPlan {
+    // K/V loads of an item go through two buffer descriptors over its (batch, KV head) rows
+    // that end with the item's last tile (or the cache length, if shorter): loads of positions
+    // past that end, and every load of an invalid item, read zeros.  A tile is then a byte
+    // offset into them.  A plan for one tile is worked out on the scalar unit; its NDMA loads
+    // per wave are issued one by one.
+    struct ItemDma {
         u32x4 rk, rv;
-        uint32_t sk, sv;
+        int tile0;   // the item's first key tile
     };
-    constexpr int NDMA = 2 * LDW;   // ring loads per wave per tile: K and V alternately
-    auto plan_tile_of = [&](const ItemGeo& g, int t, int slot) __attribute__((always_inline)) -> DmaPlan {
-        const int64_t k0 = (int64_t)(g.kt_begin + t) * BN;
-        int64_t keys = g.rule.L - k0;
-        keys = keys < 0 ? 0 : (keys > BN ? BN : keys);
-        if (t >= g.n_tiles || !g.w.valid) keys = 0;
-        const int bytes = (int)(keys * ROWB);
-        const int64_t base_off = keys > 0 ? k0 * ROWB : 0;
-        DmaPlan d;
-        d.rk = make_rsrc_words(g.kg + base_off, bytes);
-        d.rv = make_rsrc_words(g.vg + base_off, bytes);
-        const uint32_t so = (uint32_t)(slot & (STAGES - 1)) * TILE_BYTES;
-        d.sk = lds_base + so;
-        d.sv = lds_base + V_REGION + so;
+    auto item_dma = [&](const ItemGeo& g) __attribute__((always_inline)) -> ItemDma {
+        int64_t keys_end = (int64_t)(g.kt_begin + g.n_tiles) * BN;
+        if (keys_end > g.rule.L) keys_end = g.rule.L;
+        if (!g.w.valid || g.n_tiles <= 0) keys_end = 0;
+        const int bytes = (int)(keys_end * ROWB);
+        ItemDma d;
+        d.rk = make_rsrc_words(g.kg, bytes);
+        d.rv = make_rsrc_words(g.vg, bytes);
+        d.tile0 = g.kt_begin;
         return d;
     };
+    struct DmaPlan {
+        u32x4 rk, rv;
+        uint32_t off;      // byte offset of the tile in the K and V rows
+        uint32_t sk, sv;   // LDS addresses of the ring slot's K and V halves
+    };
+    constexpr int NDMA = 2 * LDW;   // ring loads per wave per tile: K and V alternately
     // load i of this wave's share of a planned tile (1 KiB of K for even i, of V for odd i)
     auto dma_issue = [&](const DmaPlan& d, auto i_c) __attribute__((always_inline)) {
         constexpr int i = decltype(i_c)::value, j = i / 2;
         const uint32_t op = (uint32_t)__builtin_amdgcn_readfirstlane(wave * LDW + j);
-        if constexpr (i % 2 == 0) dma_lds16(d.rk, d.sk + 1024u * op, k_src[j]);
-        else dma_lds16(d.rv, d.sv + 1024u * op, v_src[j]);
+        if constexpr (i % 2 == 0) dma_lds16(d.rk, d.sk + 1024u * op, k_src[j] + d.off);
+        else dma_lds16(d.rv, d.sv + 1024u * op, v_src[j] + d.off);
     };
     auto dma_issue_all = [&](const DmaPlan& d) __attribute__((always_inline)) {
         static_for<0, NDMA>([&](auto i_c) __attribute__((always_inline)) { dma_issue(d, i_c); });
@@ -335,10 +338,18 @@ fwd16_ring_kernel(const FwdParams p) {
     // (one row block per wave: the epilogue's store count that the next item's first wait
     // allows for is then fixed)
     const bool pre_next = RB == 1 && !MASKED && nxt.w.valid && nxt.n_tiles > 0 && n_tiles > 0;
+    const ItemDma cdma = item_dma(cur);
+    const ItemDma ndma = item_dma(nxt);
     auto plan_tile = [&](int t) __attribute__((always_inline)) -> DmaPlan {
-        if (pre_next && t == t_last + 2) return plan_tile_of(nxt, 0, ring_base + t);
-        if (pre_next && t == t_last + 3) return plan_tile_of(nxt, 1, ring_base + t);
-        return plan_tile_of(cur, t, ring_base + t);
+        const bool to_next = pre_next && t > t_last + 1;
+        DmaPlan d;
+        d.rk = to_next ? ndma.rk : cdma.rk;
+        d.rv = to_next ? ndma.rv : cdma.rv;
+        d.off = (uint32_t)(to_next ? ndma.tile0 + (t - t_last - 2) : cdma.tile0 + t) * (uint32_t)TILE_BYTES;
+        const uint32_t so = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
+        d.sk = lds_base + so;
+        d.sv = lds_base + V_REGION + so;
+        return d;
     };
 
     const int key_base = kt_begin * BN;
