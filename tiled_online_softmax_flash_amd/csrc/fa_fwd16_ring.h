@@ -111,7 +111,10 @@ fwd16_ring_kernel(const FwdParams p) {
     static_assert((STAGES - 1) * TILE_BYTES + HB * ROWB + 12 * ROWB + 8 < 65536,
                   "LDS operand offsets must fit the 16-bit immediate");
 
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGES * TILE_BYTES];
+    // LDS: the K/V ring, then each wave's item table (TBL_ROUNDS rounds of 32 bytes)
+    constexpr int TBL_ROUNDS = 64;
+    constexpr int TBL_OFF = 2 * STAGES * TILE_BYTES;
+    __shared__ __attribute__((aligned(1024))) char lds[TBL_OFF + WAVES * TBL_ROUNDS * 32];
     const uint32_t lds_base = lds_addr(lds);
 
     const int tid = threadIdx.x;
@@ -179,17 +182,44 @@ fwd16_ring_kernel(const FwdParams p) {
         const char* kg;
         const char* vg;
     };
-    auto item_geo = [&](int slot) __attribute__((always_inline)) -> ItemGeo {
+    // Item table: lane i of a wave works out round r0 + i's work item, key rule and key-tile
+    // range (one vector pass for TBL_ROUNDS rounds instead of a scalar pass per round) into the
+    // wave's own table; a round reads its entry back.  Entry: b, h, qt, valid | kt_begin,
+    // n_tiles, L, base (the key rule's cache length and causal base).
+    char* const tbl = lds + TBL_OFF + wave * (TBL_ROUNDS * 32);
+    auto fill_table = [&](int r0) __attribute__((always_inline)) {
+        const int slot = slot_of_round(r0 + lane);
+        WorkItem w = decode_work(p, slot * 8 + xcd);
+        w.valid = w.valid && slot < p.items_per_xcd;
+        if (!w.valid) w.b = w.h = w.qt = 0;   // never index past the inputs
+        const KeyRule rule = make_rule(p, w.b);
+        const int64_t q0 = (int64_t)w.qt * kRingBlockRows;
+        const int64_t q_last = (q0 + kRingBlockRows < p.sq ? q0 + kRingBlockRows : p.sq) - 1;
+        const int64_t lo_wg = rule.lo(q0), hi_wg = rule.hi(q_last);
+        const int kt_begin = hi_wg >= lo_wg ? (int)(lo_wg / BN) : 0;
+        const int n_tiles = hi_wg >= lo_wg ? (int)(hi_wg / BN) - kt_begin + 1 : 0;
+        if (lane < TBL_ROUNDS) {
+            *(u32x4*)(tbl + 32 * lane) = u32x4{(uint32_t)w.b, (uint32_t)w.h, (uint32_t)w.qt, w.valid ? 1u : 0u};
+            *(u32x4*)(tbl + 32 * lane + 16) =
+                u32x4{(uint32_t)kt_begin, (uint32_t)n_tiles, (uint32_t)rule.L, (uint32_t)(int32_t)rule.base};
+        }
+    };
+    auto item_geo = [&](int r) __attribute__((always_inline)) -> ItemGeo {
+        const u32x4 e0 = *(const u32x4*)(tbl + 32 * (r & (TBL_ROUNDS - 1)));
+        const u32x4 e1 = *(const u32x4*)(tbl + 32 * (r & (TBL_ROUNDS - 1)) + 16);
         ItemGeo g;
-        g.w = decode_work(p, slot * 8 + xcd);
-        g.w.valid = g.w.valid && slot < p.items_per_xcd;
-        if (!g.w.valid) g.w.b = g.w.h = g.w.qt = 0;   // never index past the inputs
-        g.rule = make_rule(p, g.w.b);
+        g.w.b = __builtin_amdgcn_readfirstlane((int)e0[0]);
+        g.w.h = __builtin_amdgcn_readfirstlane((int)e0[1]);
+        g.w.qt = __builtin_amdgcn_readfirstlane((int)e0[2]);
+        g.w.valid = __builtin_amdgcn_readfirstlane((int)e0[3]) != 0;
+        g.kt_begin = __builtin_amdgcn_readfirstlane((int)e1[0]);
+        g.n_tiles = __builtin_amdgcn_readfirstlane((int)e1[1]);
+        g.rule.L = __builtin_amdgcn_readfirstlane((int)e1[2]);
+        g.rule.base = __builtin_amdgcn_readfirstlane((int)e1[3]);
+        g.rule.window = p.window;
+        g.rule.causal = p.causal;
         g.q0 = (int64_t)g.w.qt * kRingBlockRows;
         g.q_last = (g.q0 + kRingBlockRows < p.sq ? g.q0 + kRingBlockRows : p.sq) - 1;
-        const int64_t lo_wg = g.rule.lo(g.q0), hi_wg = g.rule.hi(g.q_last);
-        g.kt_begin = hi_wg >= lo_wg ? (int)(lo_wg / BN) : 0;
-        g.n_tiles = hi_wg >= lo_wg ? (int)(hi_wg / BN) - g.kt_begin + 1 : 0;
         const int kvh = g.w.h / p.group;
         g.kg = (const char*)p.k + ((int64_t)g.w.b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
         g.vg = (const char*)p.v + ((int64_t)g.w.b * p.kv_heads + kvh) * p.kv_capacity * ROWB;
@@ -261,9 +291,11 @@ fwd16_ring_kernel(const FwdParams p) {
     // O stores of the previous item still in flight (they count in vmcnt like loads): the
     // first ring wait of an item that was prefetched lets exactly these stay outstanding
     bool prev_stores = false;
-    ItemGeo cur = item_geo(slot_of_round(0));
+    fill_table(0);
+    ItemGeo cur = item_geo(0);
     for (int round = 0; cur.w.valid; ++round) {
-    const ItemGeo nxt = item_geo(slot_of_round(round + 1));
+    if (((round + 1) & (TBL_ROUNDS - 1)) == 0) fill_table(round + 1);   // (this round's entry is read)
+    const ItemGeo nxt = item_geo(round + 1);
     const WorkItem w = cur.w;
     const int b = w.b, h = w.h;
     const KeyRule rule = cur.rule;
@@ -285,8 +317,6 @@ fwd16_ring_kernel(const FwdParams p) {
         my_lo32[rb] = (int)(lo < 0x7fffffffLL ? lo : 0x7fffffffLL);
         my_hi32[rb] = (int)(hi > -1 ? hi : -1);
     }
-    const int64_t w_lo_min = rule.lo(wr0), w_lo_max = rule.lo(wr1);
-    const int64_t w_hi_min = rule.hi(wr0), w_hi_max = rule.hi(wr1);
 
     const int kt_begin = cur.kt_begin;
     const int n_tiles = cur.n_tiles;
@@ -392,26 +422,34 @@ fwd16_ring_kernel(const FwdParams p) {
     // the row.
     const int n_half = 2 * n_tiles;
     auto clamp32 = [](int64_t v) -> int { return (int)(v < -1 ? -1 : (v > 0x7fffffffLL ? 0x7fffffffLL : v)); };
-    const int wlo_min = __builtin_amdgcn_readfirstlane(clamp32(w_lo_min));
-    const int wlo_max = __builtin_amdgcn_readfirstlane(clamp32(w_lo_max));
-    const int whi_min = __builtin_amdgcn_readfirstlane(clamp32(w_hi_min));
-    const int whi_max = __builtin_amdgcn_readfirstlane(clamp32(w_hi_max));
-    const bool wave_live = wave_has_rows && w_lo_min <= w_hi_max;
+    // lo and hi of the wave's first and last rows, evaluated on lanes 0 and 1: as both grow
+    // with the row, they bound those of every row of the wave
+    int wlo_min, wlo_max, whi_min, whi_max;
+    {
+        const int64_t ext_row = (lane & 1) ? wr1 : wr0;
+        const int e_lo = clamp32(rule.lo(ext_row)), e_hi = clamp32(rule.hi(ext_row));
+        wlo_min = __builtin_amdgcn_readlane(e_lo, 0);
+        wlo_max = __builtin_amdgcn_readlane(e_lo, 1);
+        whi_min = __builtin_amdgcn_readlane(e_hi, 0);
+        whi_max = __builtin_amdgcn_readlane(e_hi, 1);
+    }
+    const bool wave_live = wave_has_rows && wlo_min <= whi_max;
     int ua, ub, fa, fb;
     {
-        auto fdiv = [](int64_t x) -> int64_t { return x >> 5; };      // floor(x / HB)
-        auto cdiv = [](int64_t x) -> int64_t { return -((-x) >> 5); };  // ceil(x / HB)
-        auto clip = [&](int64_t x) -> int { return (int)(x < -1 ? -1 : (x > n_half ? n_half : x)); };
+        // (bounds lie in [-1, 2^31 - 1] and key_base in [0, 2^30): no step overflows 32 bits)
+        auto fdiv = [](int x) -> int { return x >> 5; };      // floor(x / HB)
+        auto cdiv = [](int x) -> int { return -((-x) >> 5); };  // ceil(x / HB)
+        auto clip = [&](int x) -> int { return x < -1 ? -1 : (x > n_half ? n_half : x); };
         static_assert(HB == 32, "fdiv/cdiv divide by 32");
-        int64_t a = cdiv((int64_t)wlo_min - (HB - 1) - key_base);
-        int64_t z = fdiv((int64_t)whi_max - key_base);
+        int a = cdiv(wlo_min - key_base - (HB - 1));
+        int z = fdiv(whi_max - key_base);
         a = a < 0 ? 0 : a;
         z = z > n_half - 1 ? n_half - 1 : z;
         if (!wave_live) { a = 0; z = -1; }
-        ua = __builtin_amdgcn_readfirstlane(clip(a));
-        ub = __builtin_amdgcn_readfirstlane(clip(z));
-        fa = __builtin_amdgcn_readfirstlane(clip(cdiv((int64_t)wlo_max - key_base)));
-        fb = __builtin_amdgcn_readfirstlane(clip(fdiv((int64_t)whi_min - (HB - 1) - key_base)));
+        ua = clip(a);
+        ub = clip(z);
+        fa = clip(cdiv(wlo_max - key_base));
+        fb = clip(fdiv(whi_min - key_base - (HB - 1)));
     }
     // full(u) implies that the wave attends half-tile u: [fa, fb] lies inside [ua, ub]
     auto full = [&](int u) __attribute__((always_inline)) { return u >= fa && u <= fb; };
@@ -731,28 +769,28 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (!MASKED) {
             // step t runs blocks 2t+1 and 2t+2, which touch half-tiles 2t .. 2t+3; without mask
             // buffers the kinds change from step to step
-            auto fdiv2 = [](int64_t x) -> int64_t { return x >> 1; };
-            auto cdiv2 = [](int64_t x) -> int64_t { return -((-x) >> 1); };
-            auto clip = [&](int64_t x, int64_t lo, int64_t hi) -> int { return (int)(x < lo ? lo : (x > hi ? hi : x)); };
+            auto fdiv2 = [](int x) -> int { return x >> 1; };
+            auto cdiv2 = [](int x) -> int { return -((-x) >> 1); };
+            auto clip = [&](int x, int lo, int hi) -> int { return x < lo ? lo : (x > hi ? hi : x); };
             // not skip: 2t+3 >= ua and 2t <= ub; full: 2t+1 >= fa and 2t+2 <= fb
-            a0 = clip(cdiv2((int64_t)ua - 3), 0, n_steps);
-            a1 = clip(fdiv2((int64_t)ub) + 1, a0, n_steps);
-            f0 = clip(cdiv2((int64_t)fa - 1), a0, a1);
-            f1 = clip(fdiv2((int64_t)fb - 2) + 1, f0, a1);
+            a0 = clip(cdiv2(ua - 3), 0, n_steps);
+            a1 = clip(fdiv2(ub) + 1, a0, n_steps);
+            f0 = clip(cdiv2(fa - 1), a0, a1);
+            f1 = clip(fdiv2(fb - 2) + 1, f0, a1);
             a0 = __builtin_amdgcn_readfirstlane(a0);
             a1 = __builtin_amdgcn_readfirstlane(a1);
             f0 = __builtin_amdgcn_readfirstlane(f0);
             f1 = __builtin_amdgcn_readfirstlane(f1);
         } else {
-            auto fdiv4 = [](int64_t x) -> int64_t { return x >> 2; };
-            auto cdiv4 = [](int64_t x) -> int64_t { return -((-x) >> 2); };
-            auto clip = [&](int64_t x, int64_t lo, int64_t hi) -> int { return (int)(x < lo ? lo : (x > hi ? hi : x)); };
+            auto fdiv4 = [](int x) -> int { return x >> 2; };
+            auto cdiv4 = [](int x) -> int { return -((-x) >> 2); };
+            auto clip = [&](int x, int lo, int hi) -> int { return x < lo ? lo : (x > hi ? hi : x); };
             // not skip: 4p+5 >= ua and 4p <= ub
-            a0 = clip(cdiv4((int64_t)ua - 5), 0, n_pairs);
-            a1 = clip(fdiv4((int64_t)ub) + 1, a0, n_pairs);
+            a0 = clip(cdiv4(ua - 5), 0, n_pairs);
+            a1 = clip(fdiv4(ub) + 1, a0, n_pairs);
             // full: 4p+1 >= fa and 4p+4 <= fb
-            f0 = clip(cdiv4((int64_t)fa - 1), a0, a1);
-            f1 = clip(fdiv4((int64_t)fb - 4) + 1, f0, a1);
+            f0 = clip(cdiv4(fa - 1), a0, a1);
+            f1 = clip(fdiv4(fb - 4) + 1, f0, a1);
             a0 = __builtin_amdgcn_readfirstlane(a0);
             a1 = __builtin_amdgcn_readfirstlane(a1);
             f0 = __builtin_amdgcn_readfirstlane(f0);
