@@ -734,7 +734,13 @@ fwd16_ring_kernel(const FwdParams p) {
                     if constexpr ((2 * i + 1) * NMB / (2 * NDMA) == m) dma_issue(dp, i_c);   // load i after MFMA m
                 });
             };
+            // The two waves of a SIMD run the same work; at equal priority the older one (waves
+            // below WAVES / 2) wins the issue slots, runs ahead, and the younger one finishes
+            // every step alone.  Raising the younger wave's priority for the first block lets
+            // the pair finish a step together more closely.
+            if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(1);
             xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, spread);
+            if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(0);
             xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
                   [](auto) {});
         }
