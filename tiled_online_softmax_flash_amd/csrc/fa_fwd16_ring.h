@@ -76,6 +76,9 @@ __device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
     }
 }
 
+// parts of a pipelined block (see the block body)
+constexpr int kBlkPV = 1, kBlkQK = 2, kBlkSM = 4, kBlkEnd = 8;
+
 template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW, int RB>
 __global__ void __attribute__((amdgpu_flat_work_group_size(ring_threads(RB), ring_threads(RB)),
                                amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
@@ -102,7 +105,11 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NSTORE = RB * (DP / 8);        // global store instructions of a wave's epilogue
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
-    constexpr int NPRE = 4 * NDB < 12 ? 4 * NDB : 12;   // V reads a block issues for the next one
+    // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
+    // a step's mask values as well and keep fewer, so that no register spills (a spill copy of a
+    // register that an asm load has not filled yet would save stale data)
+    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? (SOFTCAP ? 6 : 8) : 12;
+    constexpr int NPRE = 4 * NDB < AHEAD ? 4 * NDB : AHEAD;   // V reads a block issues for the next one
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
     using MaskH = MaskHalf<MASKK>;
@@ -558,14 +565,21 @@ fwd16_ring_kernel(const FwdParams p) {
     // block does not attend is 0 (the masked softmax masks every element), which adds exactly 0
     // because every V row in the ring is finite (rows past the cache length arrive as zeros), and
     // scores of such a half-tile are masked away.  FULL: the softmax needs no structural mask.
-    // WITH_PV false: the ring has not yet held a V tile for half-tile u-1.
-    auto xbody = [&](auto full_c, auto with_pv_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
+    // MODE (bits kBlkPV, kBlkQK, kBlkSM) drops the parts of a block that have nothing to work
+    // on: the first block of an item has no V tile for half-tile u-1 and only masked scores for
+    // half-tile -1; in an item's last step the Q.K products (and the second block's softmax)
+    // would score half-tiles past the item.  kBlkEnd: no block follows in this item.
+    auto xbody = [&](auto full_c, auto mode_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
                      f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], vec8 (&p_prev)[RB][2], vec8 (&p_cur)[RB][2],
                      const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE], auto&& unit_hook) __attribute__((always_inline)) {
-        constexpr bool WITH_PV = decltype(with_pv_c)::value;
+        constexpr int MODE = decltype(mode_c)::value;
+        constexpr bool WITH_PV = (MODE & kBlkPV) != 0;
+        constexpr bool WITH_QK = (MODE & kBlkQK) != 0;
+        constexpr bool WITH_SM = (MODE & kBlkSM) != 0;
         constexpr int PAR = decltype(par_c)::value;
         constexpr int NPV = WITH_PV ? 2 * NDB : 0;   // V^T fragments (one per P.V MFMA per row block)
-        constexpr int NF = NPV + NKS;                // operand fragments of the block
+        constexpr int NQK = WITH_QK ? NKS : 0;       // K fragments
+        constexpr int NF = NPV + NQK;                // operand fragments of the block
         constexpr int NM = RB * NF;                  // MFMAs of the block
         // LDS operand reads, in the order the MFMAs consume them: read r < 2*NPV is half r % 2
         // of V^T fragment r / 2 (4 keys x 4 dims per transpose read), read 2*NPV + ks is K
@@ -577,16 +591,13 @@ fwd16_ring_kernel(const FwdParams p) {
         // same tile's other half (PAR 0), or the first half of the next step's V tile, which
         // sits in this step's K slot (PAR 1).  A first block without P.V (PAR 0) is followed by
         // another one and issues none.
-        constexpr int NR = 2 * NPV + NKS;
-        constexpr int AHEAD = 12;
+        constexpr int NR = 2 * NPV + NQK;
         constexpr int OFFH = PAR * HB * ROWB;
         constexpr int PRE_IN = WITH_PV ? NPRE : 0;
-        constexpr int PRE_OUT = (WITH_PV || PAR == 1) ? NPRE : 0;
+        constexpr int PRE_OUT = ((WITH_PV || PAR == 1) && (MODE & kBlkEnd) == 0) ? NPRE : 0;
         constexpr int NT = NR + PRE_OUT;
-        static_assert(PRE_IN == 0 || AHEAD <= NR,
-                      "a next-block read may only reuse a leading read's entry from the unit that consumes it on");
         u32x2 rv[NPV > 0 ? 2 * NPV : 1];
-        u32x4 rk[NKS];
+        u32x4 rk[NQK > 0 ? NQK : 1];
         auto issue = [&](auto r_c) __attribute__((always_inline)) {
             constexpr int r = decltype(r_c)::value;
             if constexpr (r < PRE_IN) {
@@ -609,11 +620,20 @@ fwd16_ring_kernel(const FwdParams p) {
             constexpr int m = decltype(m_c)::value;
             constexpr int f = m / RB, rb = m % RB;
             if constexpr (rb == 0) {
-                constexpr int last = f < NPV ? 2 * f + 1 : NPV + f;   // last read fragment f needs
-                constexpr int prev = f == 0 ? -1 : (f - 1 < NPV ? 2 * (f - 1) + 1 : NPV + f - 1);
+                // reads issued by the end of unit g: AHEAD past the last one fragment g needs,
+                // and a next-block read reuses an rpre entry only once units 0 .. g consumed it
+                constexpr auto upto_of = [](int g) constexpr -> int {
+                    const int last = g < NPV ? 2 * g + 1 : NPV + g;   // last read fragment g needs
+                    int x = last + 1 + AHEAD < NT ? last + 1 + AHEAD : NT;
+                    if (PRE_IN > 0) {
+                        const int used = g < NPV ? (2 * g + 2 < PRE_IN ? 2 * g + 2 : PRE_IN) : PRE_IN;
+                        x = x < NR + used ? x : NR + used;
+                    }
+                    return x;
+                };
                 constexpr int top = NR < AHEAD ? NR : AHEAD;
-                constexpr int from = f == 0 ? top : (prev + 1 + AHEAD < NT ? prev + 1 + AHEAD : NT);
-                constexpr int upto = last + 1 + AHEAD < NT ? last + 1 + AHEAD : NT;
+                constexpr int from = f == 0 ? top : upto_of(f - 1);
+                constexpr int upto = upto_of(f) > from ? upto_of(f) : from;
                 // the fragment is taken before this unit's reads are issued: with head dim 64 they
                 // already include the next block's leading reads, which reuse the rpre entries
                 // this unit consumes
@@ -638,31 +658,35 @@ fwd16_ring_kernel(const FwdParams p) {
                 s_nxt[rb] = Tr::mfma(__builtin_bit_cast(vec8, frag), qf[rb][ks], ks == 0 ? f32x16(0.0f) : s_nxt[rb]);
             }
             // softmax phases of the RB row blocks, interleaved (slot q: phase q / RB of row block q % RB)
-            static_for<m * 8 * RB / NM, (m + 1) * 8 * RB / NM>([&](auto q_c) __attribute__((always_inline)) {
-                constexpr int q = decltype(q_c)::value;
-                constexpr int srb = q % RB;
-                softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb]);
-            });
+            if constexpr (WITH_SM) {
+                static_for<m * 8 * RB / NM, (m + 1) * 8 * RB / NM>([&](auto q_c) __attribute__((always_inline)) {
+                    constexpr int q = decltype(q_c)::value;
+                    constexpr int srb = q % RB;
+                    softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb]);
+                });
+            }
             unit_hook(m_c);
             // units (reads, wait, MFMA, softmax phases) stay in this order: a later unit's wait
             // must not run ahead of this unit's MFMA
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (WITH_SM) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            // Keep the probabilities and the row sum inside this block: otherwise they are sunk
-            // past the rescale branch below, next to the next block's P.V products that consume
-            // them, and no longer overlap this block's MFMAs.
-            u32x4 a = __builtin_bit_cast(u32x4, p_cur[rb][0]), c = __builtin_bit_cast(u32x4, p_cur[rb][1]);
-            asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run[rb]));
-            p_cur[rb][0] = __builtin_bit_cast(vec8, a);
-            p_cur[rb][1] = __builtin_bit_cast(vec8, c);
-        }
+            for (int rb = 0; rb < RB; ++rb) {
+                // Keep the probabilities and the row sum inside this block: otherwise they are
+                // sunk past the rescale branch below, next to the next block's P.V products that
+                // consume them, and no longer overlap this block's MFMAs.
+                u32x4 a = __builtin_bit_cast(u32x4, p_cur[rb][0]), c = __builtin_bit_cast(u32x4, p_cur[rb][1]);
+                asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run[rb]));
+                p_cur[rb][0] = __builtin_bit_cast(vec8, a);
+                p_cur[rb][1] = __builtin_bit_cast(vec8, c);
+            }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            if (wave_any(st[rb].moved)) {
+            for (int rb = 0; rb < RB; ++rb) {
+                if (wave_any(st[rb].moved)) {
 #pragma unroll
-                for (int i = 0; i < NDB; ++i) o[rb][i] *= st[rb].alpha;
+                    for (int i = 0; i < NDB; ++i) o[rb][i] *= st[rb].alpha;
+                }
             }
         }
     };
@@ -692,8 +716,12 @@ fwd16_ring_kernel(const FwdParams p) {
         p_even[rb][0] = p_even[rb][1] = p_odd[rb][0] = p_odd[rb][1] = vec8((scalar)0.0f);
     }
     MaskH mask_a[2][RB], mask_b[2][RB];   // [half parity][row block]: odd half-tile first
-    auto step = [&](auto kind_c, auto with_pv_c, int t, MaskH (&mcur)[2][RB], MaskH (&mnext)[2][RB]) __attribute__((always_inline)) {
+    // PHASE 0: step -1 (Q.K of half-tiles 0 and 1, softmax of half-tile 0); 1: any other step.
+    auto step = [&](auto kind_c, auto phase_c, int t, MaskH (&mcur)[2][RB], MaskH (&mnext)[2][RB]) __attribute__((always_inline)) {
         constexpr int KIND = decltype(kind_c)::value;
+        constexpr int PHASE = decltype(phase_c)::value;
+        constexpr int MODE_A = PHASE == 0 ? kBlkQK : kBlkPV | kBlkQK | kBlkSM;
+        constexpr int MODE_B = PHASE == 0 ? kBlkQK | kBlkSM : kBlkPV | kBlkQK | kBlkSM;
         if constexpr (MASK_AHEAD) {
             load_mask_half(2 * t + 3, mnext[0]);
             load_mask_half(2 * t + 4, mnext[1]);
@@ -727,7 +755,7 @@ fwd16_ring_kernel(const FwdParams p) {
             // tile t+3's loads, spread evenly over the first block's MFMAs
             auto spread = [&](auto m_c) __attribute__((always_inline)) {
                 constexpr int m = decltype(m_c)::value;
-                constexpr int NMB = RB * ((decltype(with_pv_c)::value ? 2 * NDB : 0) + NKS);
+                constexpr int NMB = RB * (((MODE_A & kBlkPV) ? 2 * NDB : 0) + ((MODE_A & kBlkQK) ? NKS : 0));
                 static_assert(NMB >= NDMA, "one load per MFMA at most");
                 static_for<0, NDMA>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
@@ -739,9 +767,9 @@ fwd16_ring_kernel(const FwdParams p) {
             // every step alone.  Raising the younger wave's priority for the first block lets
             // the pair finish a step together more closely.
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(1);
-            xbody(F{}, with_pv_c, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, spread);
+            xbody(F{}, int_c<MODE_A>{}, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, spread);
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(0);
-            xbody(F{}, with_pv_c, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
+            xbody(F{}, int_c<MODE_B>{}, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
                   [](auto) {});
         }
         if (pre && t == -1 && prev_stores) {
@@ -759,13 +787,13 @@ fwd16_ring_kernel(const FwdParams p) {
     };
     auto run_pairs = [&](auto kind_c, int p0, int p1) __attribute__((always_inline)) {
         for (int pp = p0; pp < p1; ++pp) {
-            step(kind_c, bool_c<true>{}, 2 * pp, mask_a, mask_b);
-            step(kind_c, bool_c<true>{}, 2 * pp + 1, mask_b, mask_a);
+            step(kind_c, int_c<1>{}, 2 * pp, mask_a, mask_b);
+            step(kind_c, int_c<1>{}, 2 * pp + 1, mask_b, mask_a);
         }
     };
 
     auto run_steps = [&](auto kind_c, int t0, int t1) __attribute__((always_inline)) {
-        for (int t = t0; t < t1; ++t) step(kind_c, bool_c<true>{}, t, mask_a, mask_b);
+        for (int t = t0; t < t1; ++t) step(kind_c, int_c<1>{}, t, mask_a, mask_b);
     };
 
     if (n_tiles > 0) {
@@ -813,7 +841,7 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (MASK_AHEAD) launder_mask(mask_b[1]);
         if (!pre) __syncthreads();
         // step -1: S of half-tiles 0 and 1, softmax of half-tile 0
-        step(int_c<1>{}, bool_c<false>{}, -1, mask_b, mask_a);
+        step(int_c<1>{}, int_c<0>{}, -1, mask_b, mask_a);
         if constexpr (!MASKED) {
             run_steps(int_c<0>{}, 0, a0);
             run_steps(int_c<1>{}, a0, f0);
