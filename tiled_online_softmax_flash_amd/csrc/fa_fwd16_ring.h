@@ -173,10 +173,11 @@ fwd16_ring_kernel(const FwdParams p) {
     // workgroup with id j runs on XCD j % 8 and takes, in round r, XCD-local slot
     // r * ncu + (c or ncu - 1 - c) (c = j / 8, ncu = workgroups per XCD; the order within a
     // round alternates so that the heavy-first slot order of decode_work pairs heavy items
-    // with light ones on each CU).  While an item runs its last two ring steps, the ring slots it
-    // no longer needs receive the next item's first two K/V tiles and the next item's Q is
-    // loaded, so the next item starts without a memory round trip (unmasked variants; masked
-    // ones keep their mask buffers busy to the end and start each item afresh).
+    // with light ones on each CU).  While an item runs its last three ring steps, the ring
+    // positions past its last tile receive the next item's first three K/V tiles, and its last
+    // step loads the next item's Q, so the next item starts with tiles 0 and 1 in LDS and its
+    // first step needs no wait or barrier (unmasked variants; masked ones keep their mask buffers
+    // busy to the end and start each item afresh).
     const int xcd = blockIdx.x & 7;
     const int cu = blockIdx.x >> 3;
     const int ncu = (int)(gridDim.x >> 3);
@@ -295,9 +296,6 @@ fwd16_ring_kernel(const FwdParams p) {
     // in place: that step's own Q.K products only score half-tiles past its item, which no later
     // block reads, so they may read these registers while the loads are in flight.
     vec8 qf[RB][NKS];
-    // O stores of the previous item still in flight (they count in vmcnt like loads): the
-    // first ring wait of an item that was prefetched lets exactly these stay outstanding
-    bool prev_stores = false;
     fill_table(0);
     ItemGeo cur = item_geo(0);
     for (int round = 0; cur.w.valid; ++round) {
@@ -366,23 +364,25 @@ fwd16_ring_kernel(const FwdParams p) {
     }
 
     // The item's tile t sits at ring position ring_base + t.  A step issues ring position
-    // t + 3: the item's own tile while there is one, then (pre_next) the next item's tiles 0 and
-    // 1 at positions t_last + 2 and t_last + 3 of the last two steps, else an empty tile.
+    // t + 3: the item's own tile while there is one, then (pre_next) the next item's tiles 0, 1
+    // and 2 at positions t_last + 1 .. t_last + 3 (issued by steps t_last - 2 .. t_last; the
+    // last step's Q.K products, which score past the item, read position t_last + 1), else an
+    // empty tile.
     // steps 0 .. n_steps - 1 follow step -1; masked variants run steps in pairs (their mask
     // buffers alternate), so their step count is even
     const int n_steps = MASKED ? 2 * ((n_tiles + 1) / 2) : n_tiles;
     const int t_last = n_steps - 1;   // last ring step of the item (steps -1 .. t_last)
-    // (one row block per wave: the epilogue's store count that the next item's first wait
-    // allows for is then fixed)
-    const bool pre_next = RB == 1 && !MASKED && nxt.w.valid && nxt.n_tiles > 0 && n_tiles > 0;
+    // (one row block per wave; at least three tiles, so that positions t_last + 1 .. t_last + 3
+    // are issued by the item's own steps)
+    const bool pre_next = RB == 1 && !MASKED && nxt.w.valid && nxt.n_tiles > 0 && n_tiles >= 3;
     const ItemDma cdma = item_dma(cur);
     const ItemDma ndma = item_dma(nxt);
     auto plan_tile = [&](int t) __attribute__((always_inline)) -> DmaPlan {
-        const bool to_next = pre_next && t > t_last + 1;
+        const bool to_next = pre_next && t > t_last;
         DmaPlan d;
         d.rk = to_next ? ndma.rk : cdma.rk;
         d.rv = to_next ? ndma.rv : cdma.rv;
-        d.off = (uint32_t)(to_next ? ndma.tile0 + (t - t_last - 2) : cdma.tile0 + t) * (uint32_t)TILE_BYTES;
+        d.off = (uint32_t)(to_next ? ndma.tile0 + (t - t_last - 1) : cdma.tile0 + t) * (uint32_t)TILE_BYTES;
         const uint32_t so = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
         d.sk = lds_base + so;
         d.sv = lds_base + V_REGION + so;
@@ -722,6 +722,9 @@ fwd16_ring_kernel(const FwdParams p) {
         constexpr int PHASE = decltype(phase_c)::value;
         constexpr int MODE_A = PHASE == 0 ? kBlkQK : kBlkPV | kBlkQK | kBlkSM;
         constexpr int MODE_B = PHASE == 0 ? kBlkQK | kBlkSM : kBlkPV | kBlkQK | kBlkSM;
+        // unmasked step -1: tiles 0 .. 2 are issued and tiles 0 and 1 landed and visible before
+        // it, so it issues no loads and runs into step 0 without a wait or a barrier
+        constexpr bool EARLY = PHASE == 0 && !MASKED;
         if constexpr (MASK_AHEAD) {
             load_mask_half(2 * t + 3, mnext[0]);
             load_mask_half(2 * t + 4, mnext[1]);
@@ -754,6 +757,7 @@ fwd16_ring_kernel(const FwdParams p) {
             using F = bool_c<KIND == 2>;
             // tile t+3's loads, spread evenly over the first block's MFMAs
             auto spread = [&](auto m_c) __attribute__((always_inline)) {
+                if constexpr (EARLY) return;
                 constexpr int m = decltype(m_c)::value;
                 constexpr int NMB = RB * (((MODE_A & kBlkPV) ? 2 * NDB : 0) + ((MODE_A & kBlkQK) ? NKS : 0));
                 static_assert(NMB >= NDMA, "one load per MFMA at most");
@@ -772,18 +776,14 @@ fwd16_ring_kernel(const FwdParams p) {
             xbody(F{}, int_c<MODE_B>{}, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
                   [](auto) {});
         }
-        if (pre && t == -1 && prev_stores) {
-            // everything but tile t+3 and the previous item's O stores (issued after this
-            // item's tile t+2 = 1) landed
-            dma_wait<NDMA + NSTORE>();
-        } else {
+        if constexpr (!EARLY) {
             ring_wait();   // everything but tile t+3 landed
+            if constexpr (MASK_AHEAD) {
+                launder_mask(mnext[0]);
+                launder_mask(mnext[1]);
+            }
+            __syncthreads();
         }
-        if constexpr (MASK_AHEAD) {
-            launder_mask(mnext[0]);
-            launder_mask(mnext[1]);
-        }
-        __syncthreads();
     };
     auto run_pairs = [&](auto kind_c, int p0, int p1) __attribute__((always_inline)) {
         for (int pp = p0; pp < p1; ++pp) {
@@ -834,9 +834,10 @@ fwd16_ring_kernel(const FwdParams p) {
         if (!pre) {
             dma_issue_all(plan_tile(0));
             dma_issue_all(plan_tile(1));
-            ring_wait();   // Q, tile 0 and the mask loads before it landed
+            if constexpr (!MASKED) dma_issue_all(plan_tile(2));
+            ring_wait();   // Q, tile 0 (unmasked: and tile 1) and the mask loads before them landed
         }
-        // (prefetched: the previous item's closing wait and barrier retired Q and tile 0)
+        // (prefetched: the previous item's closing wait and barrier retired Q and tiles 0 and 1)
         launder_q();
         if constexpr (MASK_AHEAD) launder_mask(mask_b[1]);
         if (!pre) __syncthreads();
@@ -882,8 +883,7 @@ fwd16_ring_kernel(const FwdParams p) {
             }
         }
     }
-    prev_stores = wave_has_rows;
-    ring_base = pre_next ? ring_base + t_last + 2 : 0;
+    ring_base = pre_next ? ring_base + t_last + 1 : 0;
     pre = pre_next;
     cur = nxt;
     }   // items
