@@ -103,7 +103,6 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int DMA_WAVES = WAVES;
     constexpr int LDW = TILE_BYTES / 1024 / DMA_WAVES;  // 1 KiB DMA ops per loading wave per operand per tile
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
-    constexpr int NSTORE = RB * (DP / 8);        // global store instructions of a wave's epilogue
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
     // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
     // a step's mask values as well and keep fewer, so that no register spills (a spill copy of a
@@ -118,10 +117,15 @@ fwd16_ring_kernel(const FwdParams p) {
     static_assert((STAGES - 1) * TILE_BYTES + HB * ROWB + 12 * ROWB + 8 < 65536,
                   "LDS operand offsets must fit the 16-bit immediate");
 
-    // LDS: the K/V ring, then each wave's item table (TBL_ROUNDS rounds of 32 bytes)
-    constexpr int TBL_ROUNDS = 64;
+    // LDS: the K/V ring, then each wave's item table (TBL_ROUNDS rounds of 32 bytes), then each
+    // wave's output staging buffer (4 chunks of 64 lanes x 8 bytes, each padded by 64 bytes so
+    // that the 16 rows x 4 chunks one read-back half-wave touches fill all 64 banks)
+    constexpr int TBL_ROUNDS = 32;
     constexpr int TBL_OFF = 2 * STAGES * TILE_BYTES;
-    __shared__ __attribute__((aligned(1024))) char lds[TBL_OFF + WAVES * TBL_ROUNDS * 32];
+    constexpr int STG_CHUNK = 64 * 8 + 64;
+    constexpr int STG_OFF = TBL_OFF + WAVES * TBL_ROUNDS * 32;
+    __shared__ __attribute__((aligned(1024))) char lds[STG_OFF + WAVES * 4 * STG_CHUNK];
+    static_assert(sizeof(lds) <= 160 * 1024, "LDS budget of one workgroup");
     const uint32_t lds_base = lds_addr(lds);
 
     const int tid = threadIdx.x;
@@ -859,26 +863,39 @@ fwd16_ring_kernel(const FwdParams p) {
     }
     if (!pre_next) dma_wait<0>();   // nothing of this item's ring stays in flight
 
-    // A wave with any valid row issues all NSTORE stores (invalid lanes masked off); a wave
-    // without one issues none.
+    // Output: O / l, rounded to 16 bits, one 32-dim block at a time through the wave's staging
+    // buffer.  Lane (m, hh) holds dims 8a + 4hh .. +3 (a = 0..3) of its row m; it writes chunk a
+    // (8 bytes) to position 'lane' of staging chunk a, and reads back, as lane 4r' + c of store
+    // s, the two halves of dims 8c .. 8c+7 of row 16s + r'.  Each store instruction then writes
+    // 64 contiguous bytes of each of 16 rows (written directly, every instruction would write 16
+    // bytes of each of 32 rows, which costs the memory pipeline about twice as long per byte).
+    // The stores are non-temporal: nothing reads the output again here.  A wave without a valid
+    // row stores nothing; rows past sq are skipped lane by lane.
     if (wave_has_rows) {
+        char* const stg = lds + STG_OFF + wave * (4 * STG_CHUNK);
+        const int rs = lane >> 2, cs = lane & 3;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const float l = half_swap_sum(l_run[rb]);
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const bool ok = row_valid[rb];
-            scalar* orow = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h +
-                           (ok ? row[rb] : 0) * p.o_stride_i;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const int d = 32 * db + 8 * a + 4 * hh;
                     f32x4 val;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) val[c] = o[rb][db][4 * a + c] * inv;
-                    const vec4 pk = __builtin_convertvector(val, vec4);
-                    if (ok) *(vec4*)(orow + d) = pk;
+                    *(u32x2*)(stg + a * STG_CHUNK + lane * 8) = __builtin_bit_cast(u32x2, __builtin_convertvector(val, vec4));
+                }
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh) {
+                    const int r = 16 * sh + rs;
+                    const u32x2 lo = *(const u32x2*)(stg + cs * STG_CHUNK + r * 8);
+                    const u32x2 hi = *(const u32x2*)(stg + cs * STG_CHUNK + 256 + r * 8);
+                    const int64_t orow_i = wr0 + 32 * rb + r;
+                    scalar* const dst = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h +
+                                        orow_i * p.o_stride_i + 32 * db + 8 * cs;
+                    if (orow_i < p.sq) __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]}, (u32x4*)dst);
                 }
             }
         }
