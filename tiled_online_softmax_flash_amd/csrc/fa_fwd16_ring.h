@@ -118,13 +118,13 @@ fwd16_ring_kernel(const FwdParams p) {
                   "LDS operand offsets must fit the 16-bit immediate");
 
     // LDS: the K/V ring, then each wave's item table (TBL_ROUNDS rounds of 32 bytes), then each
-    // wave's output staging buffer (4 chunks of 64 lanes x 8 bytes, each padded by 64 bytes so
-    // that the 16 rows x 4 chunks one read-back half-wave touches fill all 64 banks)
+    // wave's output staging buffer (8 chunks of 32 lanes x 8 bytes, each padded by 32 bytes so
+    // that the 4 rows x 8 chunks one read-back half-wave touches fill all 64 banks)
     constexpr int TBL_ROUNDS = 32;
     constexpr int TBL_OFF = 2 * STAGES * TILE_BYTES;
-    constexpr int STG_CHUNK = 64 * 8 + 64;
+    constexpr int STG_CHUNK = 32 * 8 + 32;
     constexpr int STG_OFF = TBL_OFF + WAVES * TBL_ROUNDS * 32;
-    __shared__ __attribute__((aligned(1024))) char lds[STG_OFF + WAVES * 4 * STG_CHUNK];
+    __shared__ __attribute__((aligned(1024))) char lds[STG_OFF + WAVES * 8 * STG_CHUNK];
     static_assert(sizeof(lds) <= 160 * 1024, "LDS budget of one workgroup");
     const uint32_t lds_base = lds_addr(lds);
 
@@ -863,39 +863,51 @@ fwd16_ring_kernel(const FwdParams p) {
     }
     if (!pre_next) dma_wait<0>();   // nothing of this item's ring stays in flight
 
-    // Output: O / l, rounded to 16 bits, one 32-dim block at a time through the wave's staging
-    // buffer.  Lane (m, hh) holds dims 8a + 4hh .. +3 (a = 0..3) of its row m; it writes chunk a
-    // (8 bytes) to position 'lane' of staging chunk a, and reads back, as lane 4r' + c of store
-    // s, the two halves of dims 8c .. 8c+7 of row 16s + r'.  Each store instruction then writes
-    // 64 contiguous bytes of each of 16 rows (written directly, every instruction would write 16
-    // bytes of each of 32 rows, which costs the memory pipeline about twice as long per byte).
-    // The stores are non-temporal: nothing reads the output again here.  A wave without a valid
-    // row stores nothing; rows past sq are skipped lane by lane.
+    // Output: O / l, rounded to 16 bits, in whole 128-byte row pieces (64 dims) through the
+    // wave's staging buffer, 16 rows at a time.  Lane (m, hh) holds dims 32 db + 8a + 4hh .. +3
+    // (a = 0..3) of its row m.  For rows 16 H .. 16 H + 15 and dims 64 P .. 64 P + 63, the lanes of
+    // those rows write chunk c = 4 (db - 2P) + a (8 bytes) to position 16 hh + m % 16 of staging
+    // chunk c; lane 8 r' + q of store s then reads back the two halves of dims 64 P + 8q .. +7 of
+    // row 16 H + 8 s + r'.  Each store instruction writes 8 whole 128-byte row pieces (written
+    // directly from the accumulator layout, every instruction would cover 16 bytes of each of 32
+    // rows, which holds up the memory pipeline and, with non-temporal stores, splits lines).  The
+    // stores are non-temporal: nothing reads the output again here.  A wave without a valid row
+    // stores nothing; rows past sq are skipped lane by lane.
     if (wave_has_rows) {
-        char* const stg = lds + STG_OFF + wave * (4 * STG_CHUNK);
-        const int rs = lane >> 2, cs = lane & 3;
+        constexpr int NP = DP / 64;   // 64-dim pieces per row
+        char* const stg = lds + STG_OFF + wave * (8 * STG_CHUNK);
+        const int rr = lane >> 3, q = lane & 7;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const float l = half_swap_sum(l_run[rb]);
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+            for (int P = 0; P < NP; ++P) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    f32x4 val;
+                for (int H = 0; H < 2; ++H) {
+                    if ((lr >> 4) == H) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) val[c] = o[rb][db][4 * a + c] * inv;
-                    *(u32x2*)(stg + a * STG_CHUNK + lane * 8) = __builtin_bit_cast(u32x2, __builtin_convertvector(val, vec4));
-                }
+                        for (int dd = 0; dd < 2; ++dd) {
 #pragma unroll
-                for (int sh = 0; sh < 2; ++sh) {
-                    const int r = 16 * sh + rs;
-                    const u32x2 lo = *(const u32x2*)(stg + cs * STG_CHUNK + r * 8);
-                    const u32x2 hi = *(const u32x2*)(stg + cs * STG_CHUNK + 256 + r * 8);
-                    const int64_t orow_i = wr0 + 32 * rb + r;
-                    scalar* const dst = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h +
-                                        orow_i * p.o_stride_i + 32 * db + 8 * cs;
-                    if (orow_i < p.sq) __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]}, (u32x4*)dst);
+                            for (int a = 0; a < 4; ++a) {
+                                f32x4 val;
+#pragma unroll
+                                for (int c = 0; c < 4; ++c) val[c] = o[rb][2 * P + dd][4 * a + c] * inv;
+                                *(u32x2*)(stg + (4 * dd + a) * STG_CHUNK + (16 * hh + (lr & 15)) * 8) =
+                                    __builtin_bit_cast(u32x2, __builtin_convertvector(val, vec4));
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int sh = 0; sh < 2; ++sh) {
+                        const int r = 8 * sh + rr;
+                        const u32x2 lo = *(const u32x2*)(stg + q * STG_CHUNK + r * 8);
+                        const u32x2 hi = *(const u32x2*)(stg + q * STG_CHUNK + 128 + r * 8);
+                        const int64_t orow_i = wr0 + 32 * rb + 16 * H + r;
+                        scalar* const dst = (scalar*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h +
+                                            orow_i * p.o_stride_i + 64 * P + 8 * q;
+                        if (orow_i < p.sq) __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]}, (u32x4*)dst);
+                    }
                 }
             }
         }
