@@ -110,6 +110,14 @@ EDGE = {
                               softcap=3.0),
     "amp3_bf16_causal": dict(seed=45, batch=1, heads=4, kv_heads=1, sq=300, sk=300, dim=128,
                              dtype="bf16", causal=True, amp=3.0),
+    # 256-row kernel, head dim 128, token-major rows written through the output staging, last
+    # query tile ragged
+    "token_major_d128_ragged": dict(seed=46, batch=2, heads=8, kv_heads=2, sq=600, sk=600,
+                                    dim=128, dtype="bf16", out_layout="token", causal=True),
+    # 768 work items: every persistent workgroup runs several, with the next item's tiles and Q
+    # loaded during the current one's last steps; ragged last query tile
+    "many_items_per_workgroup": dict(seed=47, batch=8, heads=32, kv_heads=8, sq=520, sk=520,
+                                     dim=128, dtype="bf16", causal=True),
 }
 
 
