@@ -82,6 +82,12 @@ enum {
  * sk == 0 (or every key removed) the output rows are written as 0.  On error nothing is
  * enqueued (except FA_ERR_HIP, which reports a failed launch) and fa_last_error() describes
  * the failure.
+ *
+ * Graph capture: a call enqueues one kernel (none for an empty problem) and neither allocates,
+ * clears memory with a memset node, nor synchronises, so it may be captured into a HIP graph
+ * and replayed.  The graph keeps the pointers and sizes of the capture: a replay reads the
+ * buffers' contents at replay time.  Make one call outside capture first on each device (it
+ * queries and caches the device's compute-unit count).
  */
 int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
                    const int32_t* total_lengths, const int32_t* past_lengths, void* out,
