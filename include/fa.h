@@ -67,7 +67,7 @@ enum {
  *   past_lengths   NULL, or device int32[batch]: cache rows before this call's first query
  *   out            output in `out_layout`, elements of `dtype`, rounded to nearest even
  *   batch, sq, sk, kv_capacity >= 0; heads >= 0; kv_heads >= 1 and divides heads;
- *   sk <= kv_capacity; 1 <= dim <= 128
+ *   sk <= kv_capacity; 1 <= dim <= 128 (16-bit dtypes) or 1 <= dim <= 384 (FA_DTYPE_F32)
  *   causal         nonzero enables bottom-right aligned causal masking
  *   mask_planes    0 (no mask), 1, batch or batch*heads; nonzero needs a non-NULL mask
  *   local_window   <= 0 disables the window; otherwise keys j < cmax + 1 - local_window drop

@@ -54,6 +54,8 @@ def test_valid_arguments_pass():
     assert status(mask=16, mask_planes=1) == fa.FA_OK
     for d in (1, 7, 40, 80, 128):
         assert status(dim=d) == fa.FA_OK, d
+    for d in (129, 200, 384):   # fp32 goes up to 384
+        assert status(dim=d, dtype=fa.FA_DTYPE_F32) == fa.FA_OK, d
     assert status(softcap=50.0, local_window=1024) == fa.FA_OK
     assert status(scale=0.0) == fa.FA_OK and status(scale=-1.0) == fa.FA_OK
 
@@ -62,6 +64,8 @@ def test_valid_arguments_pass():
     (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
     (dict(dim=0), fa.FA_ERR_UNSUPPORTED),
     (dict(dim=129), fa.FA_ERR_UNSUPPORTED),
+    (dict(dim=129, dtype=fa.FA_DTYPE_F16), fa.FA_ERR_UNSUPPORTED),
+    (dict(dim=385, dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(mask=16, mask_planes=2, mask_dtype=fa.FA_DTYPE_F16), fa.FA_ERR_UNSUPPORTED),
     (dict(out_layout=2), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(batch=-1), fa.FA_ERR_INVALID_ARGUMENT),

@@ -118,6 +118,17 @@ EDGE = {
     # loaded during the current one's last steps; ragged last query tile
     "many_items_per_workgroup": dict(seed=47, batch=8, heads=32, kv_heads=8, sq=520, sk=520,
                                      dim=128, dtype="bf16", causal=True),
+    # fp32 head dims 129..384 (three 128-dim groups; dims past D in the last group unused)
+    "fp32_d384_gqa_causal_lengths": dict(seed=50, batch=2, heads=4, kv_heads=2, sq=150, sk=170,
+                                         dim=384, dtype="f32", causal=True, lengths="past",
+                                         max_past=20),
+    "fp32_d200_window": dict(seed=51, batch=1, heads=3, kv_heads=1, sq=100, sk=260, dim=200,
+                             dtype="f32", causal=True, local_window=70),
+    "fp32_d300_mask_softcap": dict(seed=52, batch=2, heads=2, kv_heads=2, sq=70, sk=100, dim=300,
+                                   dtype="f32", mask="bernoulli", mask_p=0.2, dead_rows=3,
+                                   softcap=3.0),
+    "fp32_d129_token_major": dict(seed=53, batch=2, heads=3, kv_heads=3, sq=65, sk=65, dim=129,
+                                  dtype="f32", out_layout="token"),
 }
 
 

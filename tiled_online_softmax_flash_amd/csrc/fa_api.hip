@@ -48,6 +48,7 @@ struct Plan {
     int grid;
     int maskk;  // 0 none, 1 fp32 mask, 2 mask of the input type
     bool ring;  // 256-row LDS-ring kernel (16-bit, head dim 64/128, aligned rows)
+    bool wide;  // fp32 kernel for head dims 129..384
     bool empty;
 };
 
@@ -58,8 +59,10 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     g_error[0] = '\0';
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
         return fail(FA_ERR_UNSUPPORTED, "dtype %d is not one of F32 (0), F16 (1), BF16 (2)", dtype);
-    if (dim < 1 || dim > 128)
-        return fail(FA_ERR_UNSUPPORTED, "head dim %d outside the supported range 1..128", dim);
+    // fp32 goes up to the pages' wide variant (384); the 16-bit kernels to 128
+    const int max_dim = dtype == FA_DTYPE_F32 ? 384 : 128;
+    if (dim < 1 || dim > max_dim)
+        return fail(FA_ERR_UNSUPPORTED, "head dim %d outside the supported range 1..%d for this dtype", dim, max_dim);
     if (out_layout != FA_OUT_HEAD_MAJOR && out_layout != FA_OUT_TOKEN_MAJOR)
         return fail(FA_ERR_INVALID_ARGUMENT, "out_layout %d is neither head-major (0) nor token-major (1)", out_layout);
     if (batch < 0 || heads < 0 || sq < 0 || sk < 0 || kv_capacity < 0)
@@ -108,7 +111,8 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     plan->ring = dtype != FA_DTYPE_F32 && (dim == 64 || dim == 128) && aligned(q, 16) &&
                  aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16))) &&
                  (mask_planes == 0 || mask_vec) && (int64_t)kv_capacity * dim * 2 < 0x7fffffffLL;
-    const int block_rows = plan->ring ? fa::kRingBlockRows : fa::kBlockRows;
+    plan->wide = dtype == FA_DTYPE_F32 && dim > 128;
+    const int block_rows = plan->ring ? fa::kRingBlockRows : (plan->wide ? fa::kWideRows : fa::kBlockRows);
     if (mask_planes > 0 && (int64_t)block_rows * sk * 4 >= 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "sk %d is too long for a masked launch (a workgroup's mask rows "
                     "must span less than 2 GiB)", sk);
@@ -160,7 +164,7 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     else p.kfac = 1.4426950408889634f;                                        // x in natural units
     if (!std::isfinite(p.kfac) || !(p.kfac > 0.0f))
         return fail(FA_ERR_UNSUPPORTED, "softcap %g is too large for fp32 exponent scaling", (double)softcap);
-    plan->dp = (dim + 31) / 32 * 32;
+    plan->dp = plan->wide ? 384 : (dim + 31) / 32 * 32;
     plan->grid = (int)grid;
     return FA_OK;
 }
@@ -229,6 +233,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
     else if (dtype == FA_DTYPE_F16)
         err = plan.ring ? fa::launch_f16_ring(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s)
                         : fa::launch_f16(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s);
+    else if (plan.wide) err = fa::launch_f32_wide(p, grid, plan.maskk != 0, p.softcap > 0.0f, s);
     else err = fa::launch_f32(p, plan.dp, grid, plan.maskk != 0, p.softcap > 0.0f, s);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;

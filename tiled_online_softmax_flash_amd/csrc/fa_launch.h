@@ -10,6 +10,8 @@ namespace fa {
 hipError_t launch_bf16(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
 hipError_t launch_f16(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
 hipError_t launch_f32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s);
+// fp32, head dims 129..384
+hipError_t launch_f32_wide(const FwdParams& p, int grid, bool masked, bool softcap, hipStream_t s);
 // 256-row, 512-thread kernels for head dims 64 and 128 with 16-byte aligned rows.
 hipError_t launch_bf16_ring(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
 hipError_t launch_f16_ring(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);

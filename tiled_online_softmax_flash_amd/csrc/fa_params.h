@@ -9,6 +9,9 @@ namespace fa {
 constexpr int kBlockRows = 128;
 constexpr int kWaveRows = 32;
 constexpr int kThreads = 256;
+// fp32 kernel for head dims 129..384 (fa_fwd32w.h): 64 rows per workgroup, six waves
+constexpr int kWideRows = 64;
+constexpr int kWideThreads = 384;
 
 // Lazy rescaling threshold, in log2 units: the running row maximum is only moved when a
 // new score exceeds it by more than this, so unnormalised probabilities stay <= 2^8.

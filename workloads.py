@@ -210,7 +210,10 @@ def make_problem(
     )
 
 
-# The five named workloads at full size.  Seeds are the workload's ordinal (1..5).
+# The five named workloads at full size.  Seeds are the workload's ordinal (1..5).  A sixth,
+# vae_decoder, exercises the wide fp32 head dim (384) of the pictor page's second build of its
+# joint-attention kernel; the page gives no shape for it, so it takes a 64 x 64 latent (4096
+# tokens) with four heads, non-causal, token-major output like the DiT workload.
 WORKLOADS = {
     "tiny": dict(seed=1, batch=1, heads=1, kv_heads=1, sq=64, sk=64, dim=64, dtype="f32"),
     "dit_joint": dict(
@@ -229,6 +232,10 @@ WORKLOADS = {
         seed=5, batch=2, heads=16, kv_heads=16, sq=4096, sk=4096, dim=64, dtype="bf16",
         mask="bernoulli", mask_p=0.1, dead_rows=4,
     ),
+    "vae_decoder": dict(
+        seed=6, batch=1, heads=4, kv_heads=4, sq=4096, sk=4096, dim=384, dtype="f32",
+        out_layout="token",
+    ),
 }
 
 # Reduced copies with the same structure (dtype, features, GQA group, layout), small enough for
@@ -242,6 +249,7 @@ SMALL_WORKLOADS = {
         local_window=160, max_past=400,
     ),
     "masked_long": dict(WORKLOADS["masked_long"], heads=4, kv_heads=4, sq=261, sk=390),
+    "vae_decoder": dict(WORKLOADS["vae_decoder"], heads=2, kv_heads=2, sq=200, sk=200),
 }
 
 
