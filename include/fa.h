@@ -31,6 +31,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -105,6 +106,47 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* mask,
                   int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
                   int causal, int mask_planes, int local_window, float scale, float softcap,
                   int dtype, int mask_dtype, int out_layout);
+
+/*
+ * flash_attn_fwd_splitkv — the operation of flash_attn_fwd (same arguments, same result up to
+ * rounding order) for few query rows per KV head, such as decode steps: the key range is cut
+ * into `num_splits` spans processed in parallel, and a second kernel merges the spans' partial
+ * states (running maximum, denominator, unnormalised output) exactly as the online softmax
+ * merges tiles.  The onnx-runtime-ep-cuda page gates one-query calls of its prefill kernel to a
+ * separate decode kernel (`supported`, and the decode parity test it names); this is that path.
+ *
+ *   Takes:    dtype FA_DTYPE_BF16 or FA_DTYPE_F16, dim 64 or 128, (heads / kv_heads) * sq <= 32
+ *             (the query rows of one KV head form one 32-row block), no mask (mask_planes 0),
+ *             16-byte aligned q, k, v and out, and kv_capacity * dim * 2 < 2^31.  Anything else
+ *             returns FA_ERR_UNSUPPORTED; flash_attn_fwd covers it.
+ *   num_splits  a positive multiple of 4 (fa_splitkv_suggested_splits gives one that fills the
+ *             device); spans are ceil(sk / 32 / num_splits) 32-key tiles long.
+ *   workspace   caller-owned device memory, 16-byte aligned, at least
+ *             fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits) bytes; overwritten,
+ *             and in use until the call's work on `stream` has finished.  Calls that overlap in
+ *             time must not share a workspace.
+ *
+ * Enqueues two kernels on `stream` (none for an empty problem); no allocation, memset or
+ * synchronisation, so it may be captured into a HIP graph like flash_attn_fwd.  Errors: those
+ * of flash_attn_fwd, FA_ERR_UNSUPPORTED as above, FA_ERR_INVALID_ARGUMENT for num_splits or a
+ * missing, misaligned or short workspace, FA_ERR_OVERFLOW when the workspace size or grid
+ * overflows.
+ */
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const void* mask,
+                           const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                           int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity,
+                           int dim, int causal, int mask_planes, int local_window, float scale,
+                           float softcap, int dtype, int mask_dtype, int out_layout,
+                           int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes flash_attn_fwd_splitkv needs: num_splits * batch * kv_heads * 32 rows of
+ * (dim + 2) floats.  0 for invalid arguments or on overflow.  Host only. */
+size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_splits);
+
+/* A num_splits for flash_attn_fwd_splitkv that gives the current device about two workgroups
+ * per compute unit (a multiple of 4, at most one span per 32-key tile).  Queries the device's
+ * compute-unit count once (cached); no stream work. */
+int fa_splitkv_suggested_splits(int batch, int kv_heads, int sk);
 
 /* Thread-local text describing the most recent non-FA_OK status on this thread ("" if none).
  * The pointer stays valid until the next call into the library on the same thread. */

@@ -21,7 +21,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_check_args", "fa_last_error", "fa_version", "flash_attn_fwd"]
+    assert declared_functions() == ["fa_check_args", "fa_last_error", "fa_splitkv_suggested_splits",
+                                    "fa_splitkv_workspace_bytes", "fa_version", "flash_attn_fwd",
+                                    "flash_attn_fwd_splitkv"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -114,3 +116,48 @@ def test_binding_rejects_mismatched_shapes_and_dtypes():
         fa.flash_attn_fwd(q, torch.zeros(1, 2, 4, 16), torch.zeros(1, 2, 4, 16))
     with pytest.raises(ValueError):
         fa.flash_attn_fwd(q, q.double(), q.double())
+
+
+# ---- split-key (decode) entry point: its own checks, all taken before any launch
+
+def splitkv_status(num_splits=8, workspace=16, workspace_bytes=None, **over):
+    """flash_attn_fwd_splitkv's status for fake device pointers (no check dereferences them)."""
+    args = dict(GOOD, sq=1, heads=8, kv_heads=2, dim=128)
+    args.update(over)
+    if workspace_bytes is None:
+        workspace_bytes = fa.splitkv_workspace_bytes(args["batch"], args["kv_heads"], args["dim"], num_splits)
+    fa._load()   # sets the argument types
+    f = fa._lib.flash_attn_fwd_splitkv
+    return f(args["q"], args["k"], args["v"], args.get("mask"), None, None, args["out"], args["batch"],
+             args["heads"], args["kv_heads"], args["sq"], args["sk"], args["kv_capacity"], args["dim"],
+             args["causal"], args["mask_planes"], args["local_window"], args["scale"], args["softcap"],
+             args["dtype"], args["mask_dtype"], args["out_layout"], num_splits, workspace,
+             workspace_bytes, None)
+
+
+def test_splitkv_workspace_bytes():
+    assert fa.splitkv_workspace_bytes(8, 8, 128, 16) == 16 * 8 * 8 * 32 * 130 * 4
+    assert fa.splitkv_workspace_bytes(1, 1, 64, 4) == 4 * 32 * 66 * 4
+    assert fa.splitkv_workspace_bytes(1, 1, 64, 0) == 0
+    assert fa.splitkv_workspace_bytes(2**30, 2**30, 128, 4) == 0   # overflow
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=16, mask_planes=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(sq=9), fa.FA_ERR_UNSUPPORTED),                       # 4 heads per KV head x 9 rows > 32
+    (dict(q=8), fa.FA_ERR_UNSUPPORTED),                        # misaligned
+    (dict(num_splits=6), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(num_splits=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(workspace=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(workspace=24), fa.FA_ERR_INVALID_ARGUMENT),          # misaligned workspace
+    (dict(workspace_bytes=1024), fa.FA_ERR_INVALID_ARGUMENT),  # too small
+    (dict(heads=6, kv_heads=4), fa.FA_ERR_INVALID_ARGUMENT),   # shared check
+])
+def test_splitkv_rejects(over, code):
+    assert splitkv_status(**over) == code, fa.last_error()
+
+
+def test_splitkv_empty_problem_is_a_no_op():
+    assert splitkv_status(sq=0) == fa.FA_OK

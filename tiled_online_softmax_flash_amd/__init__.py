@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "flash_attn_fwd", "check_args", "last_error", "version", "FaError", "library_path",
+    "flash_attn_fwd", "flash_attn_fwd_splitkv", "splitkv_workspace_bytes", "splitkv_suggested_splits",
+    "check_args", "last_error", "version", "FaError", "library_path",
     "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_OVERFLOW", "FA_ERR_HIP",
     "FA_DTYPE_F32", "FA_DTYPE_F16", "FA_DTYPE_BF16",
 ]
@@ -69,6 +70,13 @@ def _load():
         lib = ctypes.CDLL(library_path)
         lib.flash_attn_fwd.argtypes = _ARGS + [ctypes.c_void_p]
         lib.flash_attn_fwd.restype = ctypes.c_int
+        lib.flash_attn_fwd_splitkv.argtypes = _ARGS + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                       ctypes.c_void_p]
+        lib.flash_attn_fwd_splitkv.restype = ctypes.c_int
+        lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 4
+        lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_splitkv_suggested_splits.argtypes = [ctypes.c_int] * 3
+        lib.fa_splitkv_suggested_splits.restype = ctypes.c_int
         lib.fa_check_args.argtypes = list(_ARGS)
         lib.fa_check_args.restype = ctypes.c_int
         lib.fa_last_error.argtypes = []
@@ -114,6 +122,62 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sk: Opt
     mask [planes,Sq,Sk] (fp32 or q's dtype); total/past lengths int32 [B] on the device.
     Returns out [B,H,Sq,D] (``out_layout="head"``) or [B,Sq,H*D] (``"token"``).
     """
+    args, out, stream = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
+                                 local_window, scale, softcap, out_layout, out, stream)
+    lib = _load()
+    status = lib.flash_attn_fwd(*args, stream.cuda_stream)
+    if status != FA_OK:
+        raise FaError(status, lib.fa_last_error().decode())
+    return out
+
+
+def splitkv_workspace_bytes(batch: int, kv_heads: int, dim: int, num_splits: int) -> int:
+    """Workspace bytes flash_attn_fwd_splitkv needs for num_splits key spans."""
+    return int(_load().fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits))
+
+
+def splitkv_suggested_splits(batch: int, kv_heads: int, sk: int) -> int:
+    """A span count that fills the current device (a multiple of 4)."""
+    return int(_load().fa_splitkv_suggested_splits(batch, kv_heads, sk))
+
+
+def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                           sk: Optional[int] = None,
+                           total_lengths: Optional[torch.Tensor] = None,
+                           past_lengths: Optional[torch.Tensor] = None, causal: bool = False,
+                           local_window: int = 0, scale: Optional[float] = None,
+                           softcap: float = 0.0, out_layout: str = "head",
+                           out: Optional[torch.Tensor] = None, num_splits: Optional[int] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The same attention forward with the keys split over workgroups (decode: few query rows).
+
+    Takes bf16/f16 inputs with head dim 64 or 128, (H / Hkv) * Sq <= 32 and no additive mask.
+    ``workspace`` (any dtype, contiguous, on q's device) needs splitkv_workspace_bytes(...) bytes;
+    it is allocated here when None.
+    """
+    args, out, stream = _marshal(q, k, v, sk, None, total_lengths, past_lengths, causal,
+                                 local_window, scale, softcap, out_layout, out, stream)
+    B, _, _, D = q.shape
+    Hkv, C = k.shape[1], k.shape[2]
+    if num_splits is None:
+        num_splits = splitkv_suggested_splits(B, Hkv, C if sk is None else int(sk))
+    need = splitkv_workspace_bytes(B, Hkv, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    lib = _load()
+    status = lib.flash_attn_fwd_splitkv(*args, int(num_splits), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if status != FA_OK:
+        raise FaError(status, lib.fa_last_error().decode())
+    return out
+
+
+def _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal, local_window, scale,
+             softcap, out_layout, out, stream):
+    """Checks the tensors and returns the C argument list (without the stream), out, stream."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,Hkv,C,D]")
     B, H, Sq, D = q.shape
@@ -154,11 +218,7 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sk: Opt
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    lib = _load()
-    status = lib.flash_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(total_lengths), _ptr(past_lengths), _ptr(out),
-        B, H, Hkv, Sq, sk, C, D, 1 if causal else 0, planes, int(local_window), float(scale),
-        float(softcap), _DTYPE_CODE[q.dtype], mask_dtype, layout, stream.cuda_stream)
-    if status != FA_OK:
-        raise FaError(status, lib.fa_last_error().decode())
-    return out
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(total_lengths), _ptr(past_lengths), _ptr(out),
+            B, H, Hkv, Sq, sk, C, D, 1 if causal else 0, planes, int(local_window), float(scale),
+            float(softcap), _DTYPE_CODE[q.dtype], mask_dtype, layout]
+    return args, out, stream

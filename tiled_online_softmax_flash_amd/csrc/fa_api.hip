@@ -239,6 +239,84 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
     return FA_OK;
 }
 
+size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_splits) {
+    if (batch < 0 || kv_heads < 1 || dim < 1 || num_splits < 1) return 0;
+    int64_t rows, bytes;
+    if (!count4(num_splits, batch, kv_heads, 32, &rows) || !mul_ok(rows, (int64_t)(dim + 2) * 4, &bytes)) return 0;
+    return (size_t)bytes;
+}
+
+int fa_splitkv_suggested_splits(int batch, int kv_heads, int sk) {
+    const int cus = device_cu_count();
+    const int64_t groups = (int64_t)(batch > 0 ? batch : 1) * (kv_heads > 0 ? kv_heads : 1);
+    // about two workgroups of four spans per CU, but spans of at least one 32-key tile
+    int64_t want = 4 * ((2 * (int64_t)(cus > 0 ? cus : 256) + groups - 1) / groups);
+    const int64_t tiles = ((int64_t)(sk > 0 ? sk : 1) + 31) / 32;
+    const int64_t cap = 4 * ((tiles + 3) / 4);
+    if (want > cap) want = cap;
+    if (want < 4) want = 4;
+    if (want > 4096) want = 4096;
+    return (int)want;
+}
+
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const void* mask,
+                           const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                           int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                           int causal, int mask_planes, int local_window, float scale, float softcap,
+                           int dtype, int mask_dtype, int out_layout, int num_splits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Plan plan;
+    const int st = validate(q, k, v, mask, out, batch, heads, kv_heads, sq, sk, kv_capacity, dim,
+                            mask_planes, scale, softcap, dtype, mask_dtype, out_layout, &plan);
+    if (st != FA_OK) return st;
+    if (dtype == FA_DTYPE_F32 || (dim != 64 && dim != 128))
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path takes bf16/f16 inputs with head dim 64 or 128");
+    if (mask_planes != 0)
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path takes no additive mask (use flash_attn_fwd)");
+    if ((int64_t)(heads / kv_heads) * sq > 32)
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs (heads / kv_heads) * sq <= 32, got %lld",
+                    (long long)(heads / kv_heads) * sq);
+    if (!aligned(q, 16) || !aligned(out, 16) || (sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs 16-byte aligned q, k, v and out");
+    if ((int64_t)kv_capacity * dim * 2 >= 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "a (batch, KV head) cache of %lld bytes exceeds the 2 GiB the split-key "
+                    "path addresses", (long long)kv_capacity * dim * 2);
+    if (num_splits < 4 || num_splits % 4 != 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be a positive multiple of 4, got %d", num_splits);
+    if (plan.empty) return FA_OK;
+    const size_t need = fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits);
+    if (need == 0) return fail(FA_ERR_OVERFLOW, "the split-key workspace size overflows");
+    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARGUMENT, "the split-key path needs a 16-byte aligned workspace of %zu bytes "
+                    "(got %zu at %p)", need, workspace_bytes, workspace);
+    int64_t grid1;
+    if (!mul_ok((int64_t)batch * kv_heads, num_splits / 4, &grid1) || grid1 > 0x7fffffffLL)
+        return fail(FA_ERR_OVERFLOW, "split-key grid exceeds the launch limit");
+
+    fa::FwdParams& p = plan.p;
+    p.total_lengths = total_lengths;
+    p.past_lengths = past_lengths;
+    p.causal = causal != 0;
+    p.window = local_window > 0 ? local_window : 0;
+    fa::SplitParams sp;
+    const int64_t ws_rows = (int64_t)num_splits * batch * kv_heads * 32;
+    sp.ws_o = (float*)workspace;
+    sp.ws_m = sp.ws_o + ws_rows * dim;
+    sp.ws_l = sp.ws_m + ws_rows;
+    sp.num_splits = num_splits;
+    const int64_t tiles = ((int64_t)sk + 31) / 32;
+    sp.span = (int)(((tiles + num_splits - 1) / num_splits) * 32);
+    if (sp.span < 32) sp.span = 32;
+    sp.rows = (heads / kv_heads) * sq;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, s)
+                                                  : fa::launch_f16_splitkv(p, sp, dim, s);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return FA_OK;
+}
+
 const char* fa_last_error(void) { return g_error; }
 
 const char* fa_version(void) { return "0.1.0"; }

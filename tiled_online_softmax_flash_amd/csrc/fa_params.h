@@ -43,4 +43,14 @@ struct FwdParams {
     int64_t o_stride_b, o_stride_h, o_stride_i;  // output strides in elements
 };
 
+// Split-key (decode) launches: the workspace and how the key range is cut (fa_splitkv.h).
+struct SplitParams {
+    float* ws_o;     // [num_splits][batch * kv_heads][32][dim] unnormalised outputs
+    float* ws_m;     // [num_splits][batch * kv_heads][32] running maxima (tracked units; -inf: no key)
+    float* ws_l;     // [num_splits][batch * kv_heads][32] denominators
+    int num_splits;  // a multiple of 4 (one span per wave, four waves per workgroup)
+    int span;        // keys per span, a multiple of 32
+    int rows;        // query rows per (batch, KV head) group: (heads / kv_heads) * sq <= 32
+};
+
 }  // namespace fa

@@ -1,0 +1,12 @@
+// bf16 and f16 instantiations of the split-key (decode) attention kernels.
+#include "fa_splitkv.h"
+#include "fa_launch.h"
+
+namespace fa {
+hipError_t launch_bf16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, hipStream_t s) {
+    return launch_splitkv<TraitsBF16>(p, sp, dp, s);
+}
+hipError_t launch_f16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, hipStream_t s) {
+    return launch_splitkv<TraitsF16>(p, sp, dp, s);
+}
+}  // namespace fa
