@@ -7,6 +7,10 @@ one JSON line: attention-forward TFLOP/s (4*B*H*Sq*Sk_eff*D per step over the wa
 steps), the dominant kernel's roofline (its average duration: HIP events recorded on the launch
 stream before the first and after the last of the K back-to-back timed launches, divided by K)
 and the f64 oracle timed on a bounded sample of the same workload on the host cores.
+
+The decode workload (gqa_decode) runs through flash_attn_fwd_splitkv instead: one step is its
+two kernels (spans, then merge), and the roofline is HBM-bound: the step's algorithmic bytes
+(Q, the attended K/V rows, O) over the event time of the two kernels, against 8 TB/s.
 """
 
 from __future__ import annotations
@@ -34,7 +38,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk_eff·D) + % of MI355X MFMA peak"
 KERNEL_SOURCES = ["fa_device.h", "fa_params.h", "fa_fwd16.h", "fa_fwd16_ring.h",
-                  "fa_fwd16_ring_consts.h", "fa_fwd32.h", "fa_launch.h", "fa_api.hip"]
+                  "fa_fwd16_ring_consts.h", "fa_fwd32.h", "fa_fwd32w.h", "fa_splitkv.h",
+                  "fa_launch.h", "fa_api.hip"]
 
 
 def kernel_hash() -> str:
@@ -144,9 +149,20 @@ def main(argv=None) -> int:
                       else (prob.batch, prob.sq, prob.heads * prob.dim), dtype=prob.q.dtype,
                       device="cuda")
     kw = dev.kwargs()
+    splitkv = args.workload in workloads.SPLITKV_WORKLOADS
+    if splitkv:
+        # decode: the split-key entry point with a workspace allocated once, outside the loop
+        kw.pop("mask")
+        splits = fa.splitkv_suggested_splits(prob.batch, prob.kv_heads, prob.sk)
+        ws = torch.empty(fa.splitkv_workspace_bytes(prob.batch, prob.kv_heads, prob.dim, splits),
+                         dtype=torch.uint8, device="cuda")
 
-    def step():
-        fa.flash_attn_fwd(dev.q, dev.k, dev.v, out=out, **kw)
+        def step():
+            fa.flash_attn_fwd_splitkv(dev.q, dev.k, dev.v, out=out, num_splits=splits,
+                                      workspace=ws, **kw)
+    else:
+        def step():
+            fa.flash_attn_fwd(dev.q, dev.k, dev.v, out=out, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -169,8 +185,13 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / args.steps
     value = work["flops"] / (ms_per_step * 1e-3) / 1e12
     kern_avg_ms = ev0.elapsed_time(ev1) / args.steps
-    achieved = work["flops"] / (kern_avg_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[prob.dtype]
+    if splitkv:
+        # HBM-bound: the step's algorithmic bytes over the event time of its two kernels
+        bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
+        achieved = work["bytes"] / (kern_avg_ms * 1e-3) / 1e9
+    else:
+        bound, unit, peak = "mfma", "TFLOP/s", PEAK_TFLOPS[prob.dtype]
+        achieved = work["flops"] / (kern_avg_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -191,14 +212,15 @@ def main(argv=None) -> int:
             "causal": prob.causal, "local_window": prob.local_window, "softcap": prob.softcap,
             "mask": None if prob.mask is None else list(prob.mask.shape),
             "out_layout": prob.out_layout, "sk_eff": round(work["sk_eff"], 3),
+            "entry_point": "flash_attn_fwd_splitkv" if splitkv else "flash_attn_fwd",
             "global_batch": prob.batch, "seq_len": prob.sq, "parallelism": "none (1 GPU)",
         },
-        "pct_of_peak": round(100.0 * value / peak, 2),
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS[prob.dtype], 2),
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "achieved": round(achieved, 2),
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": traffic_from_profile(args.workload),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 2),

@@ -143,9 +143,9 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
  * (dim + 2) floats.  0 for invalid arguments or on overflow.  Host only. */
 size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_splits);
 
-/* A num_splits for flash_attn_fwd_splitkv that gives the current device about two workgroups
- * per compute unit (a multiple of 4, at most one span per 32-key tile).  Queries the device's
- * compute-unit count once (cached); no stream work. */
+/* A num_splits for flash_attn_fwd_splitkv that gives the current device about one workgroup of
+ * four spans per compute unit (a multiple of 4, at most one span per 32-key tile).  Queries the
+ * device's compute-unit count once (cached); no stream work. */
 int fa_splitkv_suggested_splits(int batch, int kv_heads, int sk);
 
 /* Thread-local text describing the most recent non-FA_OK status on this thread ("" if none).

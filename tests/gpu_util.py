@@ -21,15 +21,21 @@ def say(msg: str) -> None:
     print(msg, file=sys.__stderr__, flush=True)
 
 
-def run_gpu(prob, out_fill: float | None = None) -> torch.Tensor:
-    """The problem on cuda:0 through flash_attn_fwd; returns the output on the GPU."""
+def run_gpu(prob, out_fill: float | None = None, splitkv: bool = False) -> torch.Tensor:
+    """The problem on cuda:0 through flash_attn_fwd (or flash_attn_fwd_splitkv with the device's
+    suggested number of spans); returns the output on the GPU."""
     d = prob.to("cuda")
     out = None
     if out_fill is not None:
         shape = (prob.batch, prob.heads, prob.sq, prob.dim) if prob.out_layout == "head" else (
             prob.batch, prob.sq, prob.heads * prob.dim)
         out = torch.full(shape, out_fill, dtype=prob.q.dtype, device="cuda")
-    res = fa.flash_attn_fwd(d.q, d.k, d.v, out=out, **d.kwargs())
+    kw = d.kwargs()
+    if splitkv:
+        assert kw.pop("mask") is None
+        res = fa.flash_attn_fwd_splitkv(d.q, d.k, d.v, out=out, **kw)
+    else:
+        res = fa.flash_attn_fwd(d.q, d.k, d.v, out=out, **kw)
     torch.cuda.synchronize()
     return res
 

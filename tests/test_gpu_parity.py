@@ -29,13 +29,16 @@ def test_small_workload_full_output(name):
     got = run_gpu(prob, out_fill=float("nan")).double().cpu().numpy()
     want = oracle_full(prob)
     check(got, want, prob.dtype, name)
+    if name in workloads.SPLITKV_WORKLOADS:   # also through the entry point bench.py times
+        got = run_gpu(prob, out_fill=float("nan"), splitkv=True).double().cpu().numpy()
+        check(got, want, prob.dtype, name + "/splitkv")
 
 
 @pytest.mark.parametrize("name", NAMES)
 def test_full_workload_sampled_rows(name):
     prob = workloads.workload(name)
     say(f"[gpu] full workload {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} {prob.dtype}")
-    out = run_gpu(prob, out_fill=float("nan"))
+    out = run_gpu(prob, out_fill=float("nan"), splitkv=name in workloads.SPLITKV_WORKLOADS)
     assert bool(torch.isfinite(out).all()), "non-finite values in the output"
     extra = []
     if prob.mask is not None:

@@ -249,8 +249,9 @@ size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_spli
 int fa_splitkv_suggested_splits(int batch, int kv_heads, int sk) {
     const int cus = device_cu_count();
     const int64_t groups = (int64_t)(batch > 0 ? batch : 1) * (kv_heads > 0 ? kv_heads : 1);
-    // about two workgroups of four spans per CU, but spans of at least one 32-key tile
-    int64_t want = 4 * ((2 * (int64_t)(cus > 0 ? cus : 256) + groups - 1) / groups);
+    // one workgroup of four spans per CU (its registers and LDS fit one per CU; a second round
+    // of workgroups costs more in start-up latency than it gains), spans of at least one tile
+    int64_t want = 4 * (((int64_t)(cus > 0 ? cus : 256) + groups - 1) / groups);
     const int64_t tiles = ((int64_t)(sk > 0 ? sk : 1) + 31) / 32;
     const int64_t cap = 4 * ((tiles + 3) / 4);
     if (want > cap) want = cap;

@@ -9,9 +9,11 @@
 //   * One (batch, KV head) group's query rows, all `group` query heads times sq rows (at most
 //     32), form the 32-row MFMA block, so every K/V byte read serves all heads sharing it.
 //   * The key range is cut into num_splits spans of `span` keys.  Each wave runs one span on its
-//     own: it streams the span's 32-key K/V tiles into two LDS slots of its own by
-//     buffer-to-LDS DMA (one tile ahead) and keeps the span's running maximum, denominator and
-//     unnormalised output in registers, which it writes to the workspace.
+//     own: it streams the span's 32-key K/V tiles through registers (two tiles in flight) into
+//     two LDS slots of its own, and keeps the span's running maximum, denominator and
+//     unnormalised output in registers, which it writes to the workspace.  The kernel is bound
+//     by HBM bandwidth; its registers allow one wave per SIMD, so the grid is best at one
+//     workgroup per compute unit (fa_splitkv_suggested_splits).
 //   * A second kernel merges the spans of every output row: with M the largest span maximum,
 //     O = sum_s 2^((m_s - M) k) O_s / sum_s 2^((m_s - M) k) l_s (0 when no span has a key).
 // LDS layouts, fragments and the softmax are those of the 256-row ring kernel (fa_fwd16_ring.h)
@@ -85,10 +87,10 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
     // arrive as zeros and are never read from memory
     const char* kg = (const char*)p.k + (int64_t)grp * p.kv_capacity * ROWB;
     const char* vg = (const char*)p.v + (int64_t)grp * p.kv_capacity * ROWB;
-    const u32x4 rk = make_rsrc_words(kg, (int)(rule.L * ROWB));
-    const u32x4 rv = make_rsrc_words(vg, (int)(rule.L * ROWB));
-    // DMA source offsets within a tile (the ring kernel's half-tile layouts): op j of this lane
-    // writes 16-byte chunk 64 j + lane of the K (V) tile
+    const __amdgpu_buffer_rsrc_t rkb = make_rsrc(kg, (int)(rule.L * ROWB));
+    const __amdgpu_buffer_rsrc_t rvb = make_rsrc(vg, (int)(rule.L * ROWB));
+    // source offsets within a tile (the ring kernel's half-tile layouts): load j of this lane
+    // fills 16-byte chunk 64 j + lane of the K (V) tile in LDS
     uint32_t k_src[NOPS], v_src[NOPS];
 #pragma unroll
     for (int j = 0; j < NOPS; ++j) {
@@ -103,14 +105,24 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
             v_src[j] = (uint32_t)(key * ROWB + (4 * db + c) * 16);
         }
     }
-    const uint32_t wave_lds = lds_addr(lds) + (uint32_t)(wave * WAVE_LDS);
-    auto issue = [&](int t) {
-        const uint32_t slot = wave_lds + (uint32_t)((t & 1) * SLOT);
+    // two tiles in flight in registers; a landed tile is stored to one of the wave's two LDS
+    // slots (plain loads and stores: at one wave per SIMD the registers hold more bytes in
+    // flight than buffer-to-LDS DMA into a third slot would)
+    u32x4 ra_k[NOPS], ra_v[NOPS], rb_k[NOPS], rb_v[NOPS];
+    auto load = [&](int t, u32x4 (&kk)[NOPS], u32x4 (&vv)[NOPS]) {
         const uint32_t off = (uint32_t)(t_begin + t) * (uint32_t)HALF;
 #pragma unroll
         for (int j = 0; j < NOPS; ++j) {
-            dma_lds16(rk, slot + 1024u * j, k_src[j] + off);
-            dma_lds16(rv, slot + HALF + 1024u * j, v_src[j] + off);
+            kk[j] = __builtin_amdgcn_raw_buffer_load_b128(rkb, k_src[j] + off, 0, 0);
+            vv[j] = __builtin_amdgcn_raw_buffer_load_b128(rvb, v_src[j] + off, 0, 0);
+        }
+    };
+    auto store = [&](int slot, const u32x4 (&kk)[NOPS], const u32x4 (&vv)[NOPS]) {
+        char* base = lds + wave * WAVE_LDS + slot * SLOT + lane * 16;
+#pragma unroll
+        for (int j = 0; j < NOPS; ++j) {
+            *(u32x4*)(base + 1024 * j) = kk[j];
+            *(u32x4*)(base + HALF + 1024 * j) = vv[j];
         }
     };
     const uint32_t k_base = (uint32_t)(lr * 32 + ((hh ^ ((lr >> 3) & 1)) << 4));
@@ -123,24 +135,15 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
-    if (n_tiles > 0) issue(0);
-    for (int t = 0; t < n_tiles; ++t) {
-        if (t + 1 < n_tiles) {
-            issue(t + 1);
-            dma_wait<2 * NOPS>();   // tile t landed (tile t + 1 may still be in flight)
-        } else {
-            dma_wait<0>();
-        }
-        const char* kt = lds + wave * WAVE_LDS + (t & 1) * SLOT;
+    auto compute = [&](int t, int slot) {
+        const char* kt = lds + wave * WAVE_LDS + slot * SLOT;
         const char* vt = kt + HALF;
-        // S^T = K Q^T for the tile's 32 keys
         f32x16 s = f32x16(0.0f);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const u32x4 a = *(const u32x4*)(kt + k_base + ks * 1024);
             s = Tr::mfma(__builtin_bit_cast(vec8, a), qf[ks], s);
         }
-        // softmax of the tile: element v of this lane is key k0 + 16 hh + v
         const int base = (t_begin + t) * 32 + 16 * hh;
         const int lo_rel = my_lo32 - base, hi_rel = my_hi32 - base;
         float mt = neg_inf();
@@ -169,11 +172,9 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
         vec8 pf[2];
         pf[0] = __builtin_convertvector(__builtin_shufflevector(s, s, 0, 1, 2, 3, 4, 5, 6, 7), vec8);
         pf[1] = __builtin_convertvector(__builtin_shufflevector(s, s, 8, 9, 10, 11, 12, 13, 14, 15), vec8);
-        // the denominator sums the rounded probabilities the P.V product uses
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             l_run = Tr::sum2(vec2{pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]}, l_run);
-        // O^T += V^T P^T
 #pragma unroll
         for (int f = 0; f < 2 * NDB; ++f) {
             const int j = f / NDB, db = f % NDB;
@@ -183,10 +184,26 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
                 (lds_s16x4*)(vt + v_base + db * 2048 + (8 * j + 4) * 64)));
             o[db] = Tr::mfma(__builtin_bit_cast(vec8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), pf[j], o[db]);
         }
+    };
+
+    if (n_tiles > 0) load(0, ra_k, ra_v);
+    if (n_tiles > 1) load(1, rb_k, rb_v);
+    if (n_tiles > 0) store(0, ra_k, ra_v);
+    for (int t = 0; t < n_tiles; t += 2) {
+        compute(t, 0);
+        if (t + 2 < n_tiles) load(t + 2, ra_k, ra_v);
+        if (t + 1 < n_tiles) {
+            store(1, rb_k, rb_v);
+            compute(t + 1, 1);
+            if (t + 3 < n_tiles) load(t + 3, rb_k, rb_v);
+        }
+        if (t + 2 < n_tiles) store(0, ra_k, ra_v);
     }
 
-    // this span's state of row lr: lane (lr, hh) holds dims 32 db + 8 a + 4 hh .. +3
+    // this span's state of row lr: lane (lr, hh) holds dims 32 db + 8 a + 4 hh .. +3; padding
+    // rows are not written (the merge reads rows below sp.rows only)
     const float l_row = half_swap_sum(l_run);
+    if (!row_valid) return;
     const int64_t srow = ((int64_t)split * (p.batch * p.kv_heads) + grp) * 32 + lr;
     float* const orow = sp.ws_o + srow * DP;
 #pragma unroll
@@ -222,19 +239,22 @@ splitkv_merge_kernel(const FwdParams p, const SplitParams sp) {
     const int grp = b * p.kv_heads + kvh;
     const int r = i * p.group + (h - kvh * p.group);
     const int64_t groups = (int64_t)p.batch * p.kv_heads;
+    // the loops carry no load-dependent branch, so the loads of several spans are in flight
+    // together (a span without keys has m = -inf, l = 0, O = 0 and gets weight 0)
+    const int64_t step = groups * 32;
+    const int64_t r0 = (int64_t)grp * 32 + r;
     float big = neg_inf();
-    for (int s = 0; s < sp.num_splits; ++s) big = __builtin_fmaxf(big, sp.ws_m[((int64_t)s * groups + grp) * 32 + r]);
+#pragma unroll 8
+    for (int s = 0; s < sp.num_splits; ++s) big = __builtin_fmaxf(big, sp.ws_m[r0 + s * step]);
     f32x4 acc = f32x4(0.0f);
     float den = 0.0f;
     if (big != neg_inf()) {
+#pragma unroll 8
         for (int s = 0; s < sp.num_splits; ++s) {
-            const int64_t srow = ((int64_t)s * groups + grp) * 32 + r;
-            const float ms = sp.ws_m[srow];
-            if (ms == neg_inf()) continue;   // a span without keys
-            const float wgt = exp2_hw((ms - big) * p.kfac);
+            const int64_t srow = r0 + s * step;
+            const float wgt = exp2_hw((sp.ws_m[srow] - big) * p.kfac);
             den += wgt * sp.ws_l[srow];
-            const f32x4 os = *(const f32x4*)(sp.ws_o + srow * DP + d);
-            acc += wgt * os;
+            acc += wgt * *(const f32x4*)(sp.ws_o + srow * DP + d);
         }
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;

@@ -236,6 +236,11 @@ WORKLOADS = {
         seed=6, batch=1, heads=4, kv_heads=4, sq=4096, sk=4096, dim=384, dtype="f32",
         out_layout="token",
     ),
+    # one decode step of the GQA shape (32 query heads on 8 KV heads, head dim 128) against a
+    # full 8192-row cache per sequence, 16 sequences: the split-key path's workload
+    "gqa_decode": dict(
+        seed=7, batch=16, heads=32, kv_heads=8, sq=1, sk=8192, dim=128, dtype="bf16", causal=True,
+    ),
 }
 
 # Reduced copies with the same structure (dtype, features, GQA group, layout), small enough for
@@ -250,7 +255,11 @@ SMALL_WORKLOADS = {
     ),
     "masked_long": dict(WORKLOADS["masked_long"], heads=4, kv_heads=4, sq=261, sk=390),
     "vae_decoder": dict(WORKLOADS["vae_decoder"], heads=2, kv_heads=2, sq=200, sk=200),
+    "gqa_decode": dict(WORKLOADS["gqa_decode"], batch=3, heads=8, kv_heads=2, sk=1000),
 }
+
+# workloads that bench.py runs through the split-key entry point
+SPLITKV_WORKLOADS = {"gqa_decode"}
 
 
 def workload(name: str, small: bool = False, **overrides) -> Problem:
