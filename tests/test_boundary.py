@@ -161,3 +161,78 @@ def test_splitkv_rejects(over, code):
 
 def test_splitkv_empty_problem_is_a_no_op():
     assert splitkv_status(sq=0) == fa.FA_OK
+
+
+# ---- sparse index selection (include/dsa.h)
+
+DSA_HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def test_dsa_header_declares_its_functions_and_the_library_exports_them():
+    text = re.sub(r"/\*.*?\*/", "", open(DSA_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+    assert names == ["dsa_check_args", "dsa_index_select", "dsa_index_select_workspace_bytes"]
+    lib = ctypes.CDLL(fa.library_path)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+DSA_GOOD = dict(query=16, key=16, weights=16, bias=16, out=16, batch=2, q_seq=3, heads=4,
+                head_dim=64, key_seq=1000, top_k=64, scale=0.125, weights_scale=1.0,
+                dtype=fa.FA_DTYPE_BF16, workspace=256, workspace_bytes=None)
+
+
+def dsa_status(**over):
+    a = dict(DSA_GOOD)
+    a.update(over)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = fa.dsa_workspace_bytes(a["batch"], a["q_seq"], a["key_seq"])
+    return fa.dsa_check_args(a["query"], a["key"], a["weights"], a["bias"], a["out"], a["batch"],
+                             a["q_seq"], a["heads"], a["head_dim"], a["key_seq"], a["top_k"],
+                             a["scale"], a["weights_scale"], a["dtype"], a["workspace"],
+                             a["workspace_bytes"])
+
+
+def test_dsa_workspace_bytes():
+    assert fa.dsa_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 4
+    assert fa.dsa_workspace_bytes(2, 3, 0) == 0
+    assert fa.dsa_workspace_bytes(-1, 3, 10) == 0
+    assert fa.dsa_workspace_bytes(2**30, 2**30, 2**30) == 0
+
+
+def test_dsa_valid_arguments_pass():
+    assert dsa_status() == fa.FA_OK
+    for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_F16):
+        assert dsa_status(dtype=dt) == fa.FA_OK
+    for d in (0, 1, 33, 100, 128):
+        assert dsa_status(head_dim=d) == fa.FA_OK, d
+    assert dsa_status(top_k=5000) == fa.FA_OK          # wider than the key range: -1 padding
+    assert dsa_status(heads=0, query=None, weights=None) == fa.FA_OK
+    assert dsa_status(batch=0, query=None, key=None, weights=None, bias=None, out=None, workspace=None) == fa.FA_OK
+    assert dsa_status(key_seq=0, key=None, bias=None, workspace=None) == fa.FA_OK
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=129), fa.FA_ERR_UNSUPPORTED),
+    (dict(top_k=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(weights_scale=-1.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(weights_scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(key_seq=-3), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(out=12), fa.FA_ERR_INVALID_ARGUMENT),         # int64 output not 8-byte aligned
+    (dict(bias=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(query=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(weights=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(workspace=None), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(workspace=264), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(workspace_bytes=100), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(batch=2**16, q_seq=2**16, key_seq=2**16), fa.FA_ERR_OVERFLOW),
+    (dict(batch=2**20, q_seq=2**11, key_seq=2**20, top_k=1, workspace_bytes=2**62), fa.FA_ERR_OVERFLOW),
+])
+def test_dsa_invalid_arguments_are_rejected(over, code):
+    assert dsa_status(**over) == code, fa.last_error()
+    assert fa.last_error() != ""

@@ -79,6 +79,14 @@ def _load():
         lib.fa_splitkv_suggested_splits.restype = ctypes.c_int
         lib.fa_check_args.argtypes = list(_ARGS)
         lib.fa_check_args.restype = ctypes.c_int
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        dsa_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp, ctypes.c_size_t]
+        lib.dsa_index_select.argtypes = dsa_args + [vp]
+        lib.dsa_index_select.restype = ctypes.c_int
+        lib.dsa_check_args.argtypes = dsa_args
+        lib.dsa_check_args.restype = ctypes.c_int
+        lib.dsa_index_select_workspace_bytes.argtypes = [i, i, i]
+        lib.dsa_index_select_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_last_error.argtypes = []
         lib.fa_last_error.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -170,6 +178,65 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     lib = _load()
     status = lib.flash_attn_fwd_splitkv(*args, int(num_splits), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if status != FA_OK:
+        raise FaError(status, lib.fa_last_error().decode())
+    return out
+
+
+def dsa_workspace_bytes(batch: int, q_seq: int, key_seq: int) -> int:
+    """Workspace bytes dsa_index_select needs."""
+    return int(_load().dsa_index_select_workspace_bytes(batch, q_seq, key_seq))
+
+
+def dsa_check_args(query, key, weights, bias, out, batch, q_seq, heads, head_dim, key_seq, top_k,
+                   scale, weights_scale, dtype, workspace, workspace_bytes) -> int:
+    """The C validation of dsa_index_select on raw integer addresses (no GPU needed)."""
+    return _load().dsa_check_args(query, key, weights, bias, out, batch, q_seq, heads, head_dim,
+                                  key_seq, top_k, scale, weights_scale, dtype, workspace,
+                                  workspace_bytes)
+
+
+def dsa_index_select(query: torch.Tensor, key: torch.Tensor, weights: torch.Tensor,
+                     bias: torch.Tensor, *, top_k: int, scale: float, weights_scale: float = 1.0,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Sparse index selection: int64 [B, 1, S, top_k] positions per query row.
+
+    query [B, S, H, D], key [B, T, D], weights [B, S, H] (one float dtype), bias [B, 1, S, T]
+    float32.  ``workspace`` (contiguous, on the same device, dsa_workspace_bytes(B, S, T) bytes)
+    is allocated here when None.
+    """
+    if query.dim() != 4 or key.dim() != 3 or weights.dim() != 3 or bias.dim() != 4:
+        raise ValueError("query [B,S,H,D], key [B,T,D], weights [B,S,H], bias [B,1,S,T]")
+    B, S, H, D = query.shape
+    T = key.shape[1]
+    if tuple(key.shape) != (B, T, D) or tuple(weights.shape) != (B, S, H) or tuple(bias.shape) != (B, 1, S, T):
+        raise ValueError(f"shapes q{tuple(query.shape)} k{tuple(key.shape)} w{tuple(weights.shape)} "
+                         f"bias{tuple(bias.shape)} do not match")
+    if query.dtype not in _DTYPE_CODE or key.dtype != query.dtype or weights.dtype != query.dtype:
+        raise ValueError("query, key and weights must share one dtype among float32, float16, bfloat16")
+    if bias.dtype != torch.float32:
+        raise ValueError("bias must be float32")
+    if out is None:
+        out = torch.empty((B, 1, S, int(top_k)), dtype=torch.int64, device=query.device)
+    elif out.dtype != torch.int64 or tuple(out.shape) != (B, 1, S, int(top_k)):
+        raise ValueError(f"out must be int64 [B, 1, S, top_k], got {out.dtype} {tuple(out.shape)}")
+    for t in (query, key, weights, bias, out):
+        if not t.is_cuda or not t.is_contiguous() or t.device != query.device:
+            raise ValueError("every tensor must be contiguous on query's GPU")
+    need = dsa_workspace_bytes(B, S, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != query.device:
+        raise ValueError("workspace must be a contiguous tensor on query's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device)
+    lib = _load()
+    status = lib.dsa_index_select(query.data_ptr(), key.data_ptr(), weights.data_ptr(),
+                                  bias.data_ptr(), out.data_ptr(), B, S, H, D, T, int(top_k),
+                                  float(scale), float(weights_scale), _DTYPE_CODE[query.dtype],
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  stream.cuda_stream)
     if status != FA_OK:
         raise FaError(status, lib.fa_last_error().decode())
     return out

@@ -13,7 +13,9 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "../../include/dsa.h"
 #include "../../include/fa.h"
+#include "dsa_kernels.h"
 #include "fa_launch.h"
 #include "fa_params.h"
 #include "fa_fwd16_ring_consts.h"
@@ -314,6 +316,86 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
     (void)hipGetLastError();
     const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, s)
                                                   : fa::launch_f16_splitkv(p, sp, dim, s);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return FA_OK;
+}
+
+size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq) {
+    if (batch < 0 || q_seq < 0 || key_seq < 0) return 0;
+    int64_t bytes;
+    if (!count4(batch, q_seq, key_seq, 4, &bytes)) return 0;
+    return (size_t)bytes;
+}
+
+int dsa_check_args(const void* query, const void* key, const void* weights, const float* bias,
+                   const int64_t* out, int batch, int q_seq, int heads, int head_dim, int key_seq,
+                   int top_k, float scale, float weights_scale, int dtype, const void* workspace,
+                   size_t workspace_bytes) {
+    g_error[0] = '\0';
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d is not one of FA_DTYPE_F32/F16/BF16", dtype);
+    if (batch < 0 || q_seq < 0 || heads < 0 || head_dim < 0 || key_seq < 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "negative size (batch %d, q_seq %d, heads %d, head_dim %d, key_seq %d)",
+                    batch, q_seq, heads, head_dim, key_seq);
+    if (head_dim > 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d exceeds 128", head_dim);
+    if (top_k < 1) return fail(FA_ERR_INVALID_ARGUMENT, "top_k must be >= 1, got %d", top_k);
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0, got %g", (double)scale);
+    if (!std::isfinite(weights_scale) || !(weights_scale > 0.0f))
+        return fail(FA_ERR_INVALID_ARGUMENT, "weights_scale must be finite and > 0, got %g", (double)weights_scale);
+    const int64_t esz = dtype == FA_DTYPE_F32 ? 4 : 2;
+    int64_t n, bytes;
+    if (!count4(batch, q_seq, heads, head_dim, &n) || !mul_ok(n, esz, &bytes) ||
+        !count4(batch, key_seq, head_dim, 1, &n) || !mul_ok(n, esz, &bytes) ||
+        !count4(batch, q_seq, heads, 1, &n) || !mul_ok(n, esz, &bytes) ||
+        !count4(batch, q_seq, key_seq, 4, &bytes) || !count4(batch, q_seq, top_k, 8, &bytes))
+        return fail(FA_ERR_OVERFLOW, "an element count or byte size overflows");
+    const int64_t rows = (int64_t)batch * q_seq;
+    if (rows == 0) return FA_OK;
+    if (out == nullptr || !aligned(out, 8)) return fail(FA_ERR_INVALID_ARGUMENT, "out is NULL or not 8-byte aligned");
+    if (key_seq > 0) {
+        if (bias == nullptr || !aligned(bias, 4)) return fail(FA_ERR_INVALID_ARGUMENT, "bias is NULL or not 4-byte aligned");
+        if (heads > 0 && weights == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "weights is NULL");
+        if (heads > 0 && head_dim > 0 && (query == nullptr || key == nullptr))
+            return fail(FA_ERR_INVALID_ARGUMENT, "query or key is NULL");
+        const int64_t tiles = ((int64_t)key_seq + 255) / 256;
+        int64_t grid;
+        if (!mul_ok(rows, tiles, &grid) || grid > 0x7fffffffLL)
+            return fail(FA_ERR_OVERFLOW, "scoring grid exceeds the launch limit");
+    }
+    if (rows > 0x7fffffffLL) return fail(FA_ERR_OVERFLOW, "selection grid exceeds the launch limit");
+    const size_t need = dsa_index_select_workspace_bytes(batch, q_seq, key_seq);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
+        return fail(FA_ERR_INVALID_ARGUMENT, "the index selection needs a 16-byte aligned workspace of %zu bytes "
+                    "(got %zu at %p)", need, workspace_bytes, workspace);
+    return FA_OK;
+}
+
+int dsa_index_select(const void* query, const void* key, const void* weights, const float* bias,
+                     int64_t* out, int batch, int q_seq, int heads, int head_dim, int key_seq,
+                     int top_k, float scale, float weights_scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    const int st = dsa_check_args(query, key, weights, bias, out, batch, q_seq, heads, head_dim, key_seq,
+                                  top_k, scale, weights_scale, dtype, workspace, workspace_bytes);
+    if (st != FA_OK || (int64_t)batch * q_seq == 0) return st;
+    dsa::DsaParams p;
+    p.query = query;
+    p.key = key;
+    p.weights = weights;
+    p.bias = bias;
+    p.keys = (uint32_t*)workspace;
+    p.out = out;
+    p.batch = batch;
+    p.q_seq = q_seq;
+    p.heads = heads;
+    p.head_dim = head_dim;
+    p.key_seq = key_seq;
+    p.top_k = top_k;
+    p.scale = scale;
+    p.weights_scale = weights_scale;
+    (void)hipGetLastError();
+    const hipError_t err = dsa::launch_index_select(p, dtype == FA_DTYPE_F32 ? 0 : (dtype == FA_DTYPE_F16 ? 1 : 2),
+                                                    (hipStream_t)stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;
 }

@@ -268,3 +268,98 @@ def workload(name: str, small: bool = False, **overrides) -> Problem:
     params = dict(table[name])
     params.update(overrides)
     return make_problem(name=name + ("_small" if small else ""), **params)
+
+
+# ------------------------------------------------------------------------------------------
+# Sparse index selection (the dsa_index_select.rs page): seeded inputs only, no arithmetic of
+# the operation.
+
+@dataclasses.dataclass
+class DsaProblem:
+    name: str
+    query: torch.Tensor     # [B, S, H, D]
+    key: torch.Tensor       # [B, T, D]
+    weights: torch.Tensor   # [B, S, H]
+    bias: torch.Tensor      # [B, 1, S, T] float32
+    top_k: int
+    scale: float
+    weights_scale: float
+
+    @property
+    def dtype(self) -> str:
+        return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[self.query.dtype]
+
+    def to(self, device) -> "DsaProblem":
+        return DsaProblem(self.name, self.query.to(device), self.key.to(device),
+                          self.weights.to(device), self.bias.to(device), self.top_k, self.scale,
+                          self.weights_scale)
+
+    def kwargs(self) -> dict:
+        return dict(top_k=self.top_k, scale=self.scale, weights_scale=self.weights_scale)
+
+
+def make_dsa_problem(*, name: str = "dsa", seed: int, batch: int, q_seq: int, heads: int,
+                     head_dim: int, key_seq: int, top_k: int, dtype: str, bias: str = "causal",
+                     scale: Optional[float] = None, weights_scale: float = 1.0,
+                     int_values: bool = False, hole_p: float = 0.0,
+                     overflow_keys: int = 0) -> DsaProblem:
+    """Draw one index-selection problem.
+
+    Values are N(0,1) (or, with ``int_values``, integers in [-2, 2], which make ties common).
+    ``bias``: ``"causal"`` (0 for positions up to the row's bottom-right causal limit
+    T - S + s, beyond it alternately -inf and the float32 minimum, both below -1e30),
+    ``"random"`` (N(0,1) values) or ``"zero"``; ``hole_p`` sets that fraction of positions to
+    -inf.  ``overflow_keys`` key rows are scaled by 1e30 so that their products overflow.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tdt = _TORCH_DTYPES[dtype]
+
+    def draw(shape):
+        if int_values:
+            return torch.from_numpy(rng.integers(-2, 3, size=shape).astype(np.float32)).to(tdt)
+        return torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(tdt)
+
+    query = draw((batch, q_seq, heads, head_dim))
+    key = draw((batch, key_seq, head_dim))
+    weights = draw((batch, q_seq, heads))
+    if overflow_keys and key_seq:
+        rows = rng.choice(key_seq, size=min(overflow_keys, key_seq), replace=False)
+        key = key.float()
+        key[:, rows, :] = 3e38   # products overflow to +-inf (f16 stores inf itself)
+        key = key.to(tdt)
+    if bias == "causal":
+        b = np.zeros((batch, 1, q_seq, key_seq), dtype=np.float32)
+        fill = np.where(np.arange(key_seq) % 2 == 0, -np.inf, np.finfo(np.float32).min).astype(np.float32)
+        for s in range(q_seq):
+            limit = key_seq - q_seq + s
+            b[:, 0, s, limit + 1:] = fill[limit + 1:]
+    elif bias == "random":
+        b = rng.standard_normal(size=(batch, 1, q_seq, key_seq), dtype=np.float32)
+    elif bias == "zero":
+        b = np.zeros((batch, 1, q_seq, key_seq), dtype=np.float32)
+    else:
+        raise ValueError(f"unknown bias recipe {bias!r}")
+    if hole_p:
+        b[rng.random(size=b.shape) < hole_p] = -np.inf
+    return DsaProblem(name=name, query=query, key=key, weights=weights, bias=torch.from_numpy(b),
+                      top_k=top_k, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
+                      weights_scale=weights_scale)
+
+
+# The index-selection workload: one decode step of a 64-head, 128-dim indexer over 32768 cached
+# positions for 8 sequences, keeping 2048 positions per query row (the page gives no shape; these
+# are the sizes such indexers are described with).  The small copy keeps the structure.
+DSA_WORKLOADS = {
+    "dsa_decode": dict(seed=8, batch=8, q_seq=1, heads=64, head_dim=128, key_seq=32768,
+                       top_k=2048, dtype="bf16", bias="causal"),
+}
+SMALL_DSA_WORKLOADS = {
+    "dsa_decode": dict(DSA_WORKLOADS["dsa_decode"], batch=2, heads=8, key_seq=3000, top_k=256),
+}
+
+
+def dsa_workload(name: str, small: bool = False, **overrides) -> DsaProblem:
+    table = SMALL_DSA_WORKLOADS if small else DSA_WORKLOADS
+    params = dict(table[name])
+    params.update(overrides)
+    return make_dsa_problem(name=name, **params)
