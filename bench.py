@@ -108,6 +108,95 @@ def cpu_baseline(prob, out_gpu: torch.Tensor, target_s: float):
     }
 
 
+# fp32 VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.  The scoring
+# multiplies and adds are separate instructions (the operation fixes un-fused rounding), one
+# float operation per lane each; the 157.3 TFLOP/s vector peak counts a packed fused multiply-add
+# as four.
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def bench_dsa(args) -> int:
+    """The index-selection workload: one step = one dsa_index_select call (scoring + selection)."""
+    prob = workloads.dsa_workload(args.workload)
+    B, S, H, D = prob.query.shape
+    T = prob.key.shape[1]
+    d = prob.to("cuda")
+    allowed = int((prob.bias > -1e30).sum())
+    ops = 2 * H * D * allowed   # one multiply and one add per (allowed cell, head, dim)
+    out = torch.empty((B, 1, S, prob.top_k), dtype=torch.int64, device="cuda")
+    ws = torch.empty(max(fa.dsa_workspace_bytes(B, S, T), 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.dsa_index_select(d.query, d.key, d.weights, d.bias, out=out, workspace=ws, **prob.kwargs())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    result = {
+        "metric": "DSA index selection: float32 score operations per second (2*H*D per allowed cell)",
+        "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "Tops/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": prob.dtype,
+        "data": "synthetic (seeded N(0,1) query/key/weights, causal float32 bias)",
+        "config": {"workload": args.workload, "batch": B, "q_seq": S, "heads": H, "head_dim": D,
+                   "key_seq": T, "top_k": prob.top_k, "allowed_cells": allowed,
+                   "entry_point": "dsa_index_select"},
+        "roofline": {
+            # event time of the whole step (scoring and selection kernels); the rocprofv3 summary
+            # gives each kernel's share
+            "bound": "alu",
+            "achieved": round(ops / (step_ms * 1e-3) / 1e12, 3),
+            "peak": round(PEAK_VALU_TOPS, 2),
+            "unit": "Tops/s",
+            "frac": round(ops / (step_ms * 1e-3) / 1e12 / PEAK_VALU_TOPS, 4),
+            "traffic": None,
+            "kernel_avg_us": round(step_ms * 1e3, 2),
+            "algorithmic_ops_per_launch": ops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dsa as dsa_oracle
+
+        host = out.cpu().numpy()
+        rows, t_used = 0, 0.0
+        t0 = time.perf_counter()
+        # whole query rows of the workload, one after another, until about --cpu-seconds
+        while rows < B * S and t_used < args.cpu_seconds:
+            b, s_ = divmod(rows, S)
+            sl = slice(s_, s_ + 1)
+            got = dsa_oracle.index_select(prob.query[b:b + 1, sl], prob.key[b:b + 1],
+                                          prob.weights[b:b + 1, sl], prob.bias[b:b + 1, :, sl],
+                                          **prob.kwargs())
+            assert np.array_equal(got[0, 0, 0], host[b, 0, s_]), "oracle and GPU disagree"
+            rows += 1
+            t_used = time.perf_counter() - t0
+        row_ops = 2 * H * D * float((prob.bias[:, 0].reshape(B * S, T)[:rows] > -1e30).sum())
+        result["cpu_baseline"] = {
+            "value": row_ops / t_used / 1e12, "unit": "Tops/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {B * S} query rows of the same workload, scored and selected "
+                      f"single-threaded in {t_used:.1f} s, every one equal to the GPU's",
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,7 +204,8 @@ def main(argv=None) -> int:
     # the GPU ramps its clocks over the first ~0.1-0.3 s of sustained load: the default warmup
     # (about 0.35 s of the GQA causal workload) lets the timed steps see the steady state
     ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--workload", default="gqa_causal", choices=list(workloads.WORKLOADS))
+    ap.add_argument("--workload", default="gqa_causal",
+                    choices=list(workloads.WORKLOADS) + list(workloads.DSA_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -141,6 +231,9 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "launches": args.steps}), flush=True)
         return 0
+
+    if args.workload in workloads.DSA_WORKLOADS:
+        return bench_dsa(args)
 
     prob = workloads.workload(args.workload)
     work = problem_work(prob)

@@ -41,6 +41,9 @@ CASES = {
     # no heads: every score is the bias
     "f32_no_heads": dict(seed=87, batch=1, q_seq=2, heads=0, head_dim=16, key_seq=300, top_k=10,
                          dtype="f32", bias="random"),
+    # a row longer than the selection kernel's LDS key cache (read from the workspace instead)
+    "bf16_uncached_long": dict(seed=90, batch=1, q_seq=2, heads=2, head_dim=32, key_seq=40000,
+                               top_k=1000, dtype="bf16", bias="random", hole_p=0.1),
     # many rows and a long key range
     "bf16_rows_long": dict(seed=88, batch=2, q_seq=5, heads=16, head_dim=128, key_seq=8192,
                            top_k=2048, dtype="bf16"),

@@ -12,10 +12,11 @@
 //     unsigned integer whose order is the IEEE-754 total order (never 0 for a canonical score).
 //     A workgroup covers 256 positions of one query row, so the row's query and weights are
 //     wave-uniform and come through scalar loads.
-//   * dsa_select_kernel: one workgroup per query row.  keep = min(#allowed, top_k).  The keep-th
-//     largest key is found exactly by four 8-bit radix passes (LDS histogram, block-wide
-//     descending prefix over the 256 digits).  Positions are then compacted in ascending order,
-//     256 at a time with ballot prefix counts: every key above the threshold, and the first
+//   * dsa_select_kernel: one 1024-thread workgroup per query row, the row's keys cached in LDS
+//     (up to 32768 positions).  keep = min(#allowed, top_k).  The keep-th largest key is found
+//     exactly by four 8-bit radix passes (LDS histogram, block-wide descending prefix over the
+//     256 digits).  Positions are then compacted in ascending order, 1024 at a time with ballot
+//     prefix counts: every key above the threshold, and the first
 //     keys equal to it, as many as the rank left over (ties go to the lower position).  The
 //     rest of the row is -1.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
@@ -30,7 +31,7 @@
 namespace dsa {
 
 constexpr int kScoreThreads = 256;
-constexpr int kSelectThreads = 256;
+constexpr int kSelectThreads = 1024;
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -48,49 +49,70 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// DMAX: head dims up to DMAX (32, 64 or 128) held in registers.
+// Head chunk staged in LDS: the query rows of up to kQStage / DMAX heads as float32.
+constexpr int kQStage = 8192;
+
 // The file is compiled with -ffp-contract=off, and the pragma keeps the kernel's products and
-// sums apart even where that flag is missing.
+// sums apart even where that flag is missing.  DMAX (32, 64 or 128) bounds the head dim held in
+// registers.
+//
+// Dims d >= head_dim are padded with zeros on both sides, which leaves every sum bit-identical:
+// a dot product starts at +0 and can never become -0 (x + -x is +0 under round-to-nearest), so
+// adding the +0 products of the padding changes nothing, NaN and infinities included.
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParams p) {
 #pragma clang fp contract(off)
+    __shared__ __attribute__((aligned(16))) float qs[kQStage];
+    __shared__ float wq[kQStage / DMAX];
+    constexpr int HC = kQStage / DMAX;   // heads per staged chunk
     const int64_t tiles = (p.key_seq + kScoreThreads - 1) / kScoreThreads;
     const int64_t row = (int64_t)blockIdx.x / tiles;
     const int64_t t = ((int64_t)blockIdx.x - row * tiles) * kScoreThreads + threadIdx.x;
-    if (t >= p.key_seq) return;
-    const int64_t cell = row * p.key_seq + t;
-    const float bias = p.bias[cell];
-    if (!(bias > -1e30f)) {
-        p.keys[cell] = 0u;
-        return;
-    }
-    const int64_t b = row / p.q_seq;
+    const bool inside = t < p.key_seq;
+    const int64_t cell = row * p.key_seq + (inside ? t : 0);
+    const float bias = inside ? p.bias[cell] : 0.0f;
+    const bool active = inside && bias > -1e30f;
     const int D = (int)p.head_dim;
-    const T* krow = (const T*)p.key + (b * p.key_seq + t) * p.head_dim;
+    const int64_t b = row / p.q_seq;
+    const T* krow = (const T*)p.key + (b * p.key_seq + (inside ? t : 0)) * p.head_dim;
     float kv[DMAX];
 #pragma unroll
-    for (int d = 0; d < DMAX; ++d) kv[d] = d < D ? to_f32<T>(krow[d]) : 0.0f;
+    for (int d = 0; d < DMAX; ++d) kv[d] = (active && d < D) ? to_f32<T>(krow[d]) : 0.0f;
     const T* qrow = (const T*)p.query + row * p.heads * p.head_dim;
     const T* wrow = (const T*)p.weights + row * p.heads;
     float total = 0.0f;
-    for (int64_t h = 0; h < p.heads; ++h) {
-        const T* qh = qrow + h * p.head_dim;
-        float dot = 0.0f;
+    for (int64_t h0 = 0; h0 < p.heads; h0 += HC) {
+        const int nh = (int)(p.heads - h0 < HC ? p.heads - h0 : HC);
+        __syncthreads();   // the previous chunk's reads are done
+        for (int i = threadIdx.x; i < nh * DMAX; i += kScoreThreads) {
+            const int hh = i / DMAX, dd = i - hh * DMAX;
+            qs[i] = dd < D ? to_f32<T>(qrow[(h0 + hh) * p.head_dim + dd]) : 0.0f;
+        }
+        for (int i = threadIdx.x; i < nh; i += kScoreThreads)
+            wq[i] = to_f32<T>(wrow[h0 + i]) * p.weights_scale;   // weight times weights_scale
+        __syncthreads();
+        if (active) {
+            for (int hh = 0; hh < nh; ++hh) {
+                const float* qh = qs + hh * DMAX;
+                float dot = 0.0f;
 #pragma unroll
-        for (int d = 0; d < DMAX; ++d) {
-            if (d < D) {
-                const float prod = to_f32<T>(qh[d]) * kv[d];
-                dot = dot + prod;
+                for (int d = 0; d < DMAX; d += 4) {
+                    const float4 q4 = *(const float4*)(qh + d);   // same address on every lane
+                    dot = dot + q4.x * kv[d];
+                    dot = dot + q4.y * kv[d + 1];
+                    dot = dot + q4.z * kv[d + 2];
+                    dot = dot + q4.w * kv[d + 3];
+                }
+                const float scaled = p.scale * dot;
+                const float relu = scaled > 0.0f ? scaled : 0.0f;   // NaN gives 0
+                total = total + relu * wq[hh];
             }
         }
-        const float scaled = p.scale * dot;
-        const float relu = scaled > 0.0f ? scaled : 0.0f;   // NaN gives 0
-        const float wgt = to_f32<T>(wrow[h]) * p.weights_scale;
-        total = total + relu * wgt;
     }
+    if (!inside) return;
     float score = total + bias;
     if (score != score) score = __uint_as_float(0x7fc00000u);
-    p.keys[cell] = order_key(score);
+    p.keys[cell] = active ? order_key(score) : 0u;
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
@@ -100,8 +122,9 @@ __device__ __forceinline__ int prefix_below(uint64_t mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Inclusive prefix sum over the 256 threads of the workgroup (thread order); `tot` gets the
-// total.  `wsum` is 4 ints of LDS.  Contains barriers: every thread must call it.
+// Inclusive prefix sum over the NT threads of the workgroup (thread order); `tot` gets the
+// total.  `wsum` is NT / 64 ints of LDS.  Contains barriers: every thread must call it.
+template <int NT>
 __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
@@ -113,45 +136,65 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int all = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        all += wsum[w];
+    }
     __syncthreads();
     *tot = all;
     return before + x;
 }
 
 // Exclusive count of `flag` over lower threads of the workgroup; `tot` gets the total.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_count(bool flag, int* wsum, int* tot) {
     const int wave = threadIdx.x >> 6;
     const uint64_t m = __ballot(flag);
     if (lane_id() == 0) wsum[wave] = __popcll(m);
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int all = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        all += wsum[w];
+    }
     __syncthreads();
     *tot = all;
     return before + prefix_below(m);
 }
 
+// Rows of at most kKeyCache positions are read from the workspace once and kept in LDS for
+// the radix passes and the compaction.
+constexpr int kKeyCache = 32768;
+
+template <bool CACHE>
 __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaParams p) {
+    constexpr int NT = kSelectThreads;
+    __shared__ uint32_t kc[CACHE ? kKeyCache : 1];
     __shared__ int hist[256];
-    __shared__ int wsum[4];
+    __shared__ int wsum[NT / 64];
     __shared__ int pick[2];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int64_t T = p.key_seq;
-    const uint32_t* keys = p.keys + row * T;
+    const uint32_t* gkeys = p.keys + row * T;
     int64_t* out = p.out + row * p.top_k;
+    auto key_at = [&](int64_t t) -> uint32_t { return CACHE ? kc[t] : gkeys[t]; };
 
-    // allowed positions of the row
+    // allowed positions of the row (and the row into LDS)
     int local = 0;
-    for (int64_t t = tid; t < T; t += kSelectThreads) local += keys[t] != 0u;
+#pragma unroll 4
+    for (int64_t t = tid; t < T; t += NT) {
+        const uint32_t k = gkeys[t];
+        if (CACHE) kc[t] = k;
+        local += k != 0u;
+    }
     int n_allowed;
-    block_inclusive_sum(local, wsum, &n_allowed);
+    block_inclusive_sum<NT>(local, wsum, &n_allowed);   // its barriers also publish kc
     const int64_t keep = (int64_t)n_allowed < p.top_k ? (int64_t)n_allowed : p.top_k;
-    for (int64_t s = keep + tid; s < p.top_k; s += kSelectThreads) out[s] = -1;
+    for (int64_t s = keep + tid; s < p.top_k; s += NT) out[s] = -1;
     if (keep == 0) return;
 
     // the keep-th largest key: four passes over 8-bit digits, most significant first.  Keys of
@@ -163,21 +206,22 @@ __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaPar
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        hist[tid] = 0;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int64_t t = tid; t < T; t += kSelectThreads) {
-            const uint32_t k = keys[t];
+#pragma unroll 4
+        for (int64_t t = tid; t < T; t += NT) {
+            const uint32_t k = key_at(t);
             if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
         }
         __syncthreads();
-        // thread i holds digit 255 - i: an inclusive prefix in thread order is the count of
-        // keys with this digit or a larger one
-        const int cnt = hist[255 - tid];
+        // thread i < 256 holds digit 255 - i: an inclusive prefix in thread order is the count
+        // of keys with this digit or a larger one
+        const int cnt = tid < 256 ? hist[255 - tid] : 0;
         int total;
-        const int cum = block_inclusive_sum(cnt, wsum, &total);
+        const int cum = block_inclusive_sum<NT>(cnt, wsum, &total);
         // exactly one digit (from the top) has a cumulative count that first reaches `rank`
         // (the keys that match `prefix` number at least `rank`)
-        if (cum >= rank && cum - cnt < rank) {
+        if (tid < 256 && cum >= rank && cum - cnt < rank) {
             pick[0] = 255 - tid;
             pick[1] = cum - cnt;   // keys with a larger digit
         }
@@ -190,19 +234,19 @@ __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaPar
     const uint32_t thr = prefix;
     const int ties_needed = rank;   // keys equal to the threshold to take, lowest positions first
 
-    // ascending compaction, 256 positions at a time
+    // ascending compaction, NT positions at a time
     int64_t written = 0;
     int ties_taken = 0;
-    for (int64_t base = 0; base < T && written < keep; base += kSelectThreads) {
+    for (int64_t base = 0; base < T && written < keep; base += NT) {
         const int64_t t = base + tid;
-        const uint32_t k = t < T ? keys[t] : 0u;
+        const uint32_t k = t < T ? key_at(t) : 0u;
         const bool gt = k > thr;
         const bool eq = k == thr && t < T;
         int eq_total;
-        const int eq_before = block_exclusive_count(eq, wsum, &eq_total);
+        const int eq_before = block_exclusive_count<NT>(eq, wsum, &eq_total);
         const bool take = gt || (eq && ties_taken + eq_before < ties_needed);
         int sel_total;
-        const int sel_before = block_exclusive_count(take, wsum, &sel_total);
+        const int sel_before = block_exclusive_count<NT>(take, wsum, &sel_total);
         if (take && written + sel_before < keep) out[written + sel_before] = t;   // exactly keep are taken
         written += sel_total;
         ties_taken += eq_total;
@@ -230,7 +274,10 @@ hipError_t launch_index_select(const DsaParams& p, int dtype, hipStream_t s) {
                                   : (dtype == 1 ? launch_score<_Float16>(p, s) : launch_score<uint16_t>(p, s));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(dsa_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads), 0, s, p);
+    if (p.key_seq <= kKeyCache)
+        hipLaunchKernelGGL(dsa_select_kernel<true>, dim3((unsigned)rows), dim3(kSelectThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(dsa_select_kernel<false>, dim3((unsigned)rows), dim3(kSelectThreads), 0, s, p);
     return hipGetLastError();
 }
 
