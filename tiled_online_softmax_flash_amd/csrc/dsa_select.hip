@@ -75,18 +75,56 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
     const int D = (int)p.head_dim;
     const int64_t b = row / p.q_seq;
     const T* krow = (const T*)p.key + (b * p.key_seq + (inside ? t : 0)) * p.head_dim;
+    // the key row into registers, all loads in flight together: 16-byte loads when the rows are
+    // 16-byte aligned and exactly DMAX long, else element loads at clamped (in-range) indices
     float kv[DMAX];
 #pragma unroll
-    for (int d = 0; d < DMAX; ++d) kv[d] = (active && d < D) ? to_f32<T>(krow[d]) : 0.0f;
+    for (int d = 0; d < DMAX; ++d) kv[d] = 0.0f;
+    const bool vec = D == DMAX && ((uintptr_t)p.key % 16) == 0 && (DMAX * sizeof(T)) % 16 == 0;
+    if (active && vec) {
+        constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte load
+        uint4 raw[DMAX / PER];
+#pragma unroll
+        for (int c = 0; c < DMAX / PER; ++c) raw[c] = *(const uint4*)(krow + c * PER);
+#pragma unroll
+        for (int c = 0; c < DMAX / PER; ++c) {
+            const T* e = (const T*)&raw[c];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) kv[c * PER + j] = to_f32<T>(e[j]);
+        }
+    } else if (active && D > 0) {
+        T raw[DMAX];
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d) raw[d] = krow[d < D ? d : D - 1];
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d) kv[d] = d < D ? to_f32<T>(raw[d]) : 0.0f;
+    }
     const T* qrow = (const T*)p.query + row * p.heads * p.head_dim;
     const T* wrow = (const T*)p.weights + row * p.heads;
     float total = 0.0f;
     for (int64_t h0 = 0; h0 < p.heads; h0 += HC) {
         const int nh = (int)(p.heads - h0 < HC ? p.heads - h0 : HC);
         __syncthreads();   // the previous chunk's reads are done
-        for (int i = threadIdx.x; i < nh * DMAX; i += kScoreThreads) {
+        // all of this thread's loads in flight together, at clamped (in-range) indices
+        constexpr int PER_T = kQStage / kScoreThreads;
+        T raw[PER_T];
+        if (D > 0) {
+#pragma unroll
+            for (int j = 0; j < PER_T; ++j) {
+                const int i = (int)threadIdx.x + j * kScoreThreads;
+                const int hh = i / DMAX, dd = i - hh * DMAX;
+                const int64_t idx = (hh < nh && dd < D) ? (h0 + hh) * p.head_dim + dd : 0;
+                raw[j] = qrow[idx];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER_T; ++j) raw[j] = (T)0;
+        }
+#pragma unroll
+        for (int j = 0; j < PER_T; ++j) {
+            const int i = (int)threadIdx.x + j * kScoreThreads;
             const int hh = i / DMAX, dd = i - hh * DMAX;
-            qs[i] = dd < D ? to_f32<T>(qrow[(h0 + hh) * p.head_dim + dd]) : 0.0f;
+            qs[i] = (hh < nh && dd < D) ? to_f32<T>(raw[j]) : 0.0f;
         }
         for (int i = threadIdx.x; i < nh; i += kScoreThreads)
             wq[i] = to_f32<T>(wrow[h0 + i]) * p.weights_scale;   // weight times weights_scale
