@@ -10,15 +10,15 @@
 //     bias.  A NaN result becomes the canonical quiet NaN.  It writes one 32-bit key per cell:
 //     0 for a position the bias removes (bias <= -1e30), otherwise the score mapped to an
 //     unsigned integer whose order is the IEEE-754 total order (never 0 for a canonical score).
-//     A workgroup covers 256 positions of one query row, so the row's query and weights are
-//     wave-uniform and come through scalar loads.
+//     A workgroup covers 256 positions of one query row; the row's query is staged in LDS as
+//     float32 and read by broadcast loads.
 //   * dsa_select_kernel: one 1024-thread workgroup per query row, the row's keys cached in LDS
 //     (up to 32768 positions).  keep = min(#allowed, top_k).  The keep-th largest key is found
 //     exactly by four 8-bit radix passes (LDS histogram, block-wide descending prefix over the
-//     256 digits).  Positions are then compacted in ascending order, 1024 at a time with ballot
-//     prefix counts: every key above the threshold, and the first
-//     keys equal to it, as many as the rank left over (ties go to the lower position).  The
-//     rest of the row is -1.
+//     256 digits).  Positions are then compacted in ascending order, each thread owning a
+//     contiguous run of positions and two block prefix sums placing its winners: every key
+//     above the threshold, and the first keys equal to it, as many as the rank left over (ties
+//     go to the lower position).  The rest of the row is -1.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -133,9 +133,14 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
             for (int hh = 0; hh < nh; ++hh) {
                 const float* qh = qs + hh * DMAX;
                 float dot = 0.0f;
+                // query reads (same address on every lane) requested two groups ahead of use
+                float4 qa = *(const float4*)(qh);
+                float4 qb = *(const float4*)(qh + 4);
 #pragma unroll
                 for (int d = 0; d < DMAX; d += 4) {
-                    const float4 q4 = *(const float4*)(qh + d);   // same address on every lane
+                    const float4 q4 = qa;
+                    qa = qb;
+                    if (d + 8 < DMAX) qb = *(const float4*)(qh + d + 8);
                     dot = dot + q4.x * kv[d];
                     dot = dot + q4.y * kv[d + 1];
                     dot = dot + q4.z * kv[d + 2];
@@ -154,11 +159,6 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
-
-// number of set bits of a 64-lane ballot below this lane
-__device__ __forceinline__ int prefix_below(uint64_t mask) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 // Inclusive prefix sum over the NT threads of the workgroup (thread order); `tot` gets the
 // total.  `wsum` is NT / 64 ints of LDS.  Contains barriers: every thread must call it.
@@ -185,32 +185,16 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     return before + x;
 }
 
-// Exclusive count of `flag` over lower threads of the workgroup; `tot` gets the total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_count(bool flag, int* wsum, int* tot) {
-    const int wave = threadIdx.x >> 6;
-    const uint64_t m = __ballot(flag);
-    if (lane_id() == 0) wsum[wave] = __popcll(m);
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        before += w < wave ? wsum[w] : 0;
-        all += wsum[w];
-    }
-    __syncthreads();
-    *tot = all;
-    return before + prefix_below(m);
-}
-
 // Rows of at most kKeyCache positions are read from the workspace once and kept in LDS for
-// the radix passes and the compaction.
+// the radix passes and the compaction, with one padding word after every 32 keys so that
+// threads walking contiguous 32-key runs hit distinct banks.
 constexpr int kKeyCache = 32768;
+__device__ __forceinline__ int64_t cache_index(int64_t t) { return t + (t >> 5); }
 
 template <bool CACHE>
 __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaParams p) {
     constexpr int NT = kSelectThreads;
-    __shared__ uint32_t kc[CACHE ? kKeyCache : 1];
+    __shared__ uint32_t kc[CACHE ? kKeyCache + kKeyCache / 32 : 1];
     __shared__ int hist[256];
     __shared__ int wsum[NT / 64];
     __shared__ int pick[2];
@@ -219,14 +203,14 @@ __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaPar
     const int64_t T = p.key_seq;
     const uint32_t* gkeys = p.keys + row * T;
     int64_t* out = p.out + row * p.top_k;
-    auto key_at = [&](int64_t t) -> uint32_t { return CACHE ? kc[t] : gkeys[t]; };
+    auto key_at = [&](int64_t t) -> uint32_t { return CACHE ? kc[cache_index(t)] : gkeys[t]; };
 
     // allowed positions of the row (and the row into LDS)
     int local = 0;
 #pragma unroll 4
     for (int64_t t = tid; t < T; t += NT) {
         const uint32_t k = gkeys[t];
-        if (CACHE) kc[t] = k;
+        if (CACHE) kc[cache_index(t)] = k;
         local += k != 0u;
     }
     int n_allowed;
@@ -272,22 +256,37 @@ __global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaPar
     const uint32_t thr = prefix;
     const int ties_needed = rank;   // keys equal to the threshold to take, lowest positions first
 
-    // ascending compaction, NT positions at a time
-    int64_t written = 0;
+    // ascending compaction: thread i owns the contiguous positions [i C, (i + 1) C).  It counts
+    // its keys above and equal to the threshold; block prefix sums give it the ties it may take
+    // (the lowest positions first) and its first output slot; it then writes its winners in
+    // position order.
+    const int64_t C = (T + NT - 1) / NT;
+    const int64_t c0 = (int64_t)tid * C;
+    const int64_t c1 = c0 + C < T ? c0 + C : T;
+    int gt_n = 0, eq_n = 0;
+    for (int64_t t = c0; t < c1; ++t) {
+        const uint32_t k = key_at(t);
+        gt_n += k > thr;
+        eq_n += k == thr;
+    }
+    int total;
+    const int eq_before = block_inclusive_sum<NT>(eq_n, wsum, &total) - eq_n;
+    int my_ties = ties_needed - eq_before;
+    my_ties = my_ties < 0 ? 0 : (my_ties > eq_n ? eq_n : my_ties);
+    const int sel = gt_n + my_ties;
+    int64_t slot = block_inclusive_sum<NT>(sel, wsum, &total) - sel;
     int ties_taken = 0;
-    for (int64_t base = 0; base < T && written < keep; base += NT) {
-        const int64_t t = base + tid;
-        const uint32_t k = t < T ? key_at(t) : 0u;
-        const bool gt = k > thr;
-        const bool eq = k == thr && t < T;
-        int eq_total;
-        const int eq_before = block_exclusive_count<NT>(eq, wsum, &eq_total);
-        const bool take = gt || (eq && ties_taken + eq_before < ties_needed);
-        int sel_total;
-        const int sel_before = block_exclusive_count<NT>(take, wsum, &sel_total);
-        if (take && written + sel_before < keep) out[written + sel_before] = t;   // exactly keep are taken
-        written += sel_total;
-        ties_taken += eq_total;
+    for (int64_t t = c0; t < c1; ++t) {
+        const uint32_t k = key_at(t);
+        bool take = k > thr;
+        if (k == thr && ties_taken < my_ties) {
+            take = true;
+            ++ties_taken;
+        }
+        if (take) {
+            if (slot < keep) out[slot] = t;   // exactly keep are taken
+            ++slot;
+        }
     }
 }
 
