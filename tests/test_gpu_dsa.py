@@ -143,3 +143,17 @@ def test_dsa_graph_replay():
         assert torch.equal(out, eager), f"replay {rep}"
     want = dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs())
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_dsa_on_a_side_stream():
+    """The call runs on the stream it is given; results read after that stream is synchronised."""
+    prob = workloads.make_dsa_problem(name="side", **CASES["bf16_decode_d128"])
+    d = prob.to("cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # inputs were copied on the default stream
+    say("[gpu] dsa side stream")
+    with torch.cuda.stream(side):
+        out = fa.dsa_index_select(d.query, d.key, d.weights, d.bias, stream=side, **prob.kwargs())
+    side.synchronize()
+    want = dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs())
+    assert np.array_equal(out.cpu().numpy(), want)

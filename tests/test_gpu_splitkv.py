@@ -119,3 +119,16 @@ def test_splitkv_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
     check(out.double().cpu().numpy(), oracle_full(prob), "bf16", "graph")
+
+
+def test_splitkv_on_a_side_stream():
+    prob = workloads.make_problem(name="side", **CASES["f16_d64_softcap_window"])
+    d = prob.to("cuda")
+    kw = _kwargs(prob)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # inputs were copied on the default stream
+    say("[gpu] splitkv side stream")
+    with torch.cuda.stream(side):
+        out = fa.flash_attn_fwd_splitkv(d.q, d.k, d.v, num_splits=8, stream=side, **kw)
+    side.synchronize()
+    check(out.double().cpu().numpy(), oracle_full(prob), prob.dtype, "side-stream")
