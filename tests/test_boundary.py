@@ -208,6 +208,7 @@ def test_dsa_valid_arguments_pass():
         assert dsa_status(head_dim=d) == fa.FA_OK, d
     assert dsa_status(top_k=5000) == fa.FA_OK          # wider than the key range: -1 padding
     assert dsa_status(heads=0, query=None, weights=None) == fa.FA_OK
+    assert dsa_status(heads=0, query=None, key=None, weights=None) == fa.FA_OK   # scores = bias
     assert dsa_status(batch=0, query=None, key=None, weights=None, bias=None, out=None, workspace=None) == fa.FA_OK
     assert dsa_status(key_seq=0, key=None, bias=None, workspace=None) == fa.FA_OK
 

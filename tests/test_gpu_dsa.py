@@ -111,6 +111,26 @@ def test_dsa_small_workload_and_reuse():
     assert np.array_equal(b, dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs()))
 
 
+def test_dsa_no_heads_with_null_query_key_and_weights():
+    """With no heads the scores are the bias alone; query, key and weights may be NULL."""
+    prob = workloads.make_dsa_problem(seed=91, batch=1, q_seq=2, heads=0, head_dim=16, key_seq=300,
+                                      top_k=10, dtype="bf16", bias="random")
+    B, S, _, _ = prob.query.shape
+    T = prob.key.shape[1]
+    bias = prob.bias.to("cuda")
+    out = torch.empty((B, 1, S, prob.top_k), dtype=torch.int64, device="cuda")
+    ws = torch.empty(fa.dsa_workspace_bytes(B, S, T), dtype=torch.uint8, device="cuda")
+    say("[gpu] dsa no heads, NULL query/key/weights")
+    lib = fa._load()
+    status = lib.dsa_index_select(None, None, None, bias.data_ptr(), out.data_ptr(), B, S, 0, 16, T,
+                                  prob.top_k, prob.scale, prob.weights_scale, fa.FA_DTYPE_BF16,
+                                  ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert status == fa.FA_OK, fa.last_error()
+    torch.cuda.synchronize()
+    want = dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs())
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
 def test_dsa_no_keys_gives_minus_one():
     prob = workloads.make_dsa_problem(seed=89, batch=2, q_seq=3, heads=2, head_dim=8, key_seq=0,
                                       top_k=5, dtype="bf16")

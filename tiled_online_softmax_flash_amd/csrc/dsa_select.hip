@@ -80,8 +80,10 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
     float kv[DMAX];
 #pragma unroll
     for (int d = 0; d < DMAX; ++d) kv[d] = 0.0f;
+    // (no heads: the score is the bias alone and key may be NULL, so nothing is loaded)
+    const bool load = active && p.heads > 0;
     const bool vec = D == DMAX && ((uintptr_t)p.key % 16) == 0 && (DMAX * sizeof(T)) % 16 == 0;
-    if (active && vec) {
+    if (load && vec) {
         constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte load
         uint4 raw[DMAX / PER];
 #pragma unroll
@@ -92,7 +94,7 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
 #pragma unroll
             for (int j = 0; j < PER; ++j) kv[c * PER + j] = to_f32<T>(e[j]);
         }
-    } else if (active && D > 0) {
+    } else if (load && D > 0) {
         T raw[DMAX];
 #pragma unroll
         for (int d = 0; d < DMAX; ++d) raw[d] = krow[d < D ? d : D - 1];
