@@ -78,6 +78,13 @@ EDGE = {
     "single_key": dict(seed=29, batch=1, heads=3, kv_heads=1, sq=40, sk=1, dim=64, dtype="f16"),
     "softcap_saturating": dict(seed=30, batch=2, heads=4, kv_heads=2, sq=150, sk=200, dim=64,
                                dtype="f16", softcap=2.0, amp=3.0, causal=True),
+    # the largest softcap that takes the identity tanh, with small scores (where it has no
+    # relative accuracy), and the next one up (the series near 0)
+    "softcap_identity_limit": dict(seed=33, batch=1, heads=4, kv_heads=1, sq=130, sk=260, dim=128,
+                                   dtype="bf16", softcap=1024.0, amp=0.3, causal=True),
+    "softcap_above_identity_limit": dict(seed=34, batch=1, heads=4, kv_heads=1, sq=130, sk=260,
+                                         dim=128, dtype="f16", softcap=1025.0, amp=0.3,
+                                         causal=True),
     "softcap_huge_is_plain": dict(seed=31, batch=1, heads=2, kv_heads=1, sq=100, sk=100, dim=64,
                                   dtype="bf16", softcap=1e30),
     "softcap_with_mask": dict(seed=32, batch=2, heads=2, kv_heads=2, sq=100, sk=96, dim=64,

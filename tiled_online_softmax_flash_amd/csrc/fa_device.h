@@ -36,6 +36,16 @@ __device__ __forceinline__ float tanh_fast(float y) {
     return __builtin_fabsf(y) < 0.125f ? small : big;
 }
 
+// tanh(y) from the identity tanh y = 1 - 2 / (e^{2y} + 1) alone: absolute error a few fp32 ulps
+// of 1 everywhere (it saturates cleanly to +-1), but no relative accuracy near 0.  Scaled by a
+// softcap c <= kTanhIdentityMaxCap the capped score is off by at most about c * 2^-21 < 5e-4,
+// which leaves the softmax weights within 1e-3 relative; larger caps use tanh_fast.
+constexpr float kTanhIdentityMaxCap = 1024.0f;
+__device__ __forceinline__ float tanh_identity(float y) {
+    const float e = exp2_hw(y * (2.0f * kLog2e));
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
 // One workgroup's share of the problem: batch b, query head h, query tile qt.
 struct WorkItem {
     int b, h, qt;

@@ -79,7 +79,8 @@ __device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
 // parts of a pipelined block (see the block body)
 constexpr int kBlkPV = 1, kBlkQK = 2, kBlkSM = 4, kBlkEnd = 8;
 
-template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW, int RB>
+// SOFTCAP: 0 none, 1 tanh_fast, 2 tanh_identity (unmasked, softcap <= kTanhIdentityMaxCap).
+template <typename Tr, int DP, int MASKK, int SOFTCAP, bool RAW, int RB>
 __global__ void __attribute__((amdgpu_flat_work_group_size(ring_threads(RB), ring_threads(RB)),
                                amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
 fwd16_ring_kernel(const FwdParams p) {
@@ -468,7 +469,7 @@ fwd16_ring_kernel(const FwdParams p) {
     // score epilogue of one element: tracked units x (see RAW / SOFTCAP / MASKED)
     auto epi = [&](float sv, float mvv) __attribute__((always_inline)) -> float {
         if constexpr (SOFTCAP) {
-            const float th = tanh_fast(sv * p.cap_y);
+            const float th = SOFTCAP == 2 ? tanh_identity(sv * p.cap_y) : tanh_fast(sv * p.cap_y);
             return MASKED ? __builtin_fmaf(p.softcap, th, mvv) : th;
         } else if constexpr (MASKED) {
             return __builtin_fmaf(sv, p.scale, mvv);
@@ -920,7 +921,7 @@ fwd16_ring_kernel(const FwdParams p) {
 }
 
 
-template <typename Tr, int DP, int MASKK, bool SOFTCAP, bool RAW>
+template <typename Tr, int DP, int MASKK, int SOFTCAP, bool RAW>
 hipError_t launch_ring_one(const FwdParams& p, int grid, hipStream_t stream) {
     constexpr int RB = kRingRowBlocks;
     hipLaunchKernelGGL((fwd16_ring_kernel<Tr, DP, MASKK, SOFTCAP, RAW, RB>), dim3(grid), dim3(ring_threads(RB)), 0,
@@ -931,14 +932,15 @@ hipError_t launch_ring_one(const FwdParams& p, int grid, hipStream_t stream) {
 template <typename Tr, int DP>
 hipError_t launch_ring_dp(const FwdParams& p, int grid, int maskk, bool softcap, hipStream_t s) {
     if (softcap) {
-        if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, true, false>(p, grid, s);
-        if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, true, false>(p, grid, s);
-        return launch_ring_one<Tr, DP, kMaskNone, true, false>(p, grid, s);
+        if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 1, false>(p, grid, s);
+        if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 1, false>(p, grid, s);
+        if (p.softcap <= kTanhIdentityMaxCap) return launch_ring_one<Tr, DP, kMaskNone, 2, false>(p, grid, s);
+        return launch_ring_one<Tr, DP, kMaskNone, 1, false>(p, grid, s);
     }
-    if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, false, false>(p, grid, s);
-    if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, false, false>(p, grid, s);
-    if (p.raw_scores) return launch_ring_one<Tr, DP, kMaskNone, false, true>(p, grid, s);
-    return launch_ring_one<Tr, DP, kMaskNone, false, false>(p, grid, s);
+    if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, false>(p, grid, s);
+    if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, false>(p, grid, s);
+    if (p.raw_scores) return launch_ring_one<Tr, DP, kMaskNone, 0, true>(p, grid, s);
+    return launch_ring_one<Tr, DP, kMaskNone, 0, false>(p, grid, s);
 }
 
 template <typename Tr>
