@@ -85,6 +85,13 @@ EDGE = {
     "softcap_above_identity_limit": dict(seed=34, batch=1, heads=4, kv_heads=1, sq=130, sk=260,
                                          dim=128, dtype="f16", softcap=1025.0, amp=0.3,
                                          causal=True),
+    # a large cap with an additive mask (identity tanh, masked kernel) and one above the limit
+    "softcap_1000_with_mask": dict(seed=35, batch=2, heads=2, kv_heads=2, sq=100, sk=96, dim=64,
+                                   dtype="bf16", softcap=1000.0, amp=0.3, mask="normal",
+                                   mask_p=0.2),
+    "softcap_2000_with_mask": dict(seed=36, batch=2, heads=2, kv_heads=2, sq=100, sk=96, dim=128,
+                                   dtype="f16", softcap=2000.0, amp=0.3, mask="bernoulli",
+                                   mask_p=0.2),
     "softcap_huge_is_plain": dict(seed=31, batch=1, heads=2, kv_heads=1, sq=100, sk=100, dim=64,
                                   dtype="bf16", softcap=1e30),
     "softcap_with_mask": dict(seed=32, batch=2, heads=2, kv_heads=2, sq=100, sk=96, dim=64,

@@ -79,7 +79,7 @@ __device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
 // parts of a pipelined block (see the block body)
 constexpr int kBlkPV = 1, kBlkQK = 2, kBlkSM = 4, kBlkEnd = 8;
 
-// SOFTCAP: 0 none, 1 tanh_fast, 2 tanh_identity (unmasked, softcap <= kTanhIdentityMaxCap).
+// SOFTCAP: 0 none, 1 tanh_fast, 2 tanh_identity (softcap <= kTanhIdentityMaxCap).
 template <typename Tr, int DP, int MASKK, int SOFTCAP, bool RAW, int RB>
 __global__ void __attribute__((amdgpu_flat_work_group_size(ring_threads(RB), ring_threads(RB)),
                                amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
@@ -932,10 +932,15 @@ hipError_t launch_ring_one(const FwdParams& p, int grid, hipStream_t stream) {
 template <typename Tr, int DP>
 hipError_t launch_ring_dp(const FwdParams& p, int grid, int maskk, bool softcap, hipStream_t s) {
     if (softcap) {
-        if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 1, false>(p, grid, s);
-        if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 1, false>(p, grid, s);
-        if (p.softcap <= kTanhIdentityMaxCap) return launch_ring_one<Tr, DP, kMaskNone, 2, false>(p, grid, s);
-        return launch_ring_one<Tr, DP, kMaskNone, 1, false>(p, grid, s);
+        const bool identity = p.softcap <= kTanhIdentityMaxCap;
+        if (maskk == kMaskF32)
+            return identity ? launch_ring_one<Tr, DP, kMaskF32, 2, false>(p, grid, s)
+                            : launch_ring_one<Tr, DP, kMaskF32, 1, false>(p, grid, s);
+        if (maskk == kMaskT)
+            return identity ? launch_ring_one<Tr, DP, kMaskT, 2, false>(p, grid, s)
+                            : launch_ring_one<Tr, DP, kMaskT, 1, false>(p, grid, s);
+        return identity ? launch_ring_one<Tr, DP, kMaskNone, 2, false>(p, grid, s)
+                        : launch_ring_one<Tr, DP, kMaskNone, 1, false>(p, grid, s);
     }
     if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, false>(p, grid, s);
     if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, false>(p, grid, s);
