@@ -215,7 +215,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the op shards without "
-              "communication over (batch, KV-head) groups, see DESIGN.md", file=sys.stderr)
+              "communication over (batch, KV-head) groups, each GPU taking its own groups", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
