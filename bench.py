@@ -211,6 +211,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of attention, run --steps plain device copies of BYTES bytes "
                          "(reference for scaling FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--stream-reference", type=int, default=0, metavar="BYTES",
+                    help="instead of attention, time a plain device copy and a read-only sum of "
+                         "BYTES bytes (the streaming rates a bandwidth-bound kernel compares with)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -220,6 +223,28 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+
+    if args.stream_reference:
+        n = args.stream_reference // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        res = {"bytes": 4 * n, "launches": args.steps}
+        for name, fn, moved in (("copy", lambda: dst.copy_(src), 8 * n), ("sum", lambda: src.sum(), 4 * n)):
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            res[name] = {"us": round(us, 2), "gbs": round(moved / us / 1e3, 1),
+                         "moved_bytes": moved}
+        print(json.dumps(res), flush=True)
+        return 0
 
     if args.copy_calibration:
         n = args.copy_calibration // 4
