@@ -270,7 +270,6 @@ def main(argv=None) -> int:
     splitkv = args.workload in workloads.SPLITKV_WORKLOADS
     if splitkv:
         # decode: the split-key entry point with a workspace allocated once, outside the loop
-        kw.pop("mask")
         splits = fa.splitkv_suggested_splits(prob.batch, prob.kv_heads, prob.sk)
         ws = torch.empty(fa.splitkv_workspace_bytes(prob.batch, prob.kv_heads, prob.dim, splits),
                          dtype=torch.uint8, device="cuda")

@@ -116,8 +116,8 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* mask,
  * separate decode kernel (`supported`, and the decode parity test it names); this is that path.
  *
  *   Takes:    dtype FA_DTYPE_BF16 or FA_DTYPE_F16, dim 64 or 128, (heads / kv_heads) * sq <= 32
- *             (the query rows of one KV head form one 32-row block), no mask (mask_planes 0),
- *             16-byte aligned q, k, v and out, and kv_capacity * dim * 2 < 2^31.  Anything else
+ *             (the query rows of one KV head form one 32-row block), 16-byte aligned q, k, v and
+ *             out, and kv_capacity * dim * 2 < 2^31; masks as for flash_attn_fwd.  Anything else
  *             returns FA_ERR_UNSUPPORTED; flash_attn_fwd covers it.
  *   num_splits  a positive multiple of 4 (fa_splitkv_suggested_splits gives one that fills the
  *             device); spans are ceil(sk / 32 / num_splits) 32-key tiles long.

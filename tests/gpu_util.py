@@ -32,7 +32,6 @@ def run_gpu(prob, out_fill: float | None = None, splitkv: bool = False) -> torch
         out = torch.full(shape, out_fill, dtype=prob.q.dtype, device="cuda")
     kw = d.kwargs()
     if splitkv:
-        assert kw.pop("mask") is None
         res = fa.flash_attn_fwd_splitkv(d.q, d.k, d.v, out=out, **kw)
     else:
         res = fa.flash_attn_fwd(d.q, d.k, d.v, out=out, **kw)

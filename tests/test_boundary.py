@@ -145,7 +145,6 @@ def test_splitkv_workspace_bytes():
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(dim=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(mask=16, mask_planes=2), fa.FA_ERR_UNSUPPORTED),
     (dict(sq=9), fa.FA_ERR_UNSUPPORTED),                       # 4 heads per KV head x 9 rows > 32
     (dict(q=8), fa.FA_ERR_UNSUPPORTED),                        # misaligned
     (dict(num_splits=6), fa.FA_ERR_INVALID_ARGUMENT),
@@ -157,6 +156,13 @@ def test_splitkv_workspace_bytes():
 ])
 def test_splitkv_rejects(over, code):
     assert splitkv_status(**over) == code, fa.last_error()
+
+
+def test_splitkv_takes_masks():
+    # sq = 0: every check runs, then the empty problem returns before any launch
+    assert splitkv_status(mask=16, mask_planes=2, sq=0) == fa.FA_OK
+    assert splitkv_status(mask=16, mask_planes=16, mask_dtype=fa.FA_DTYPE_BF16, sq=0) == fa.FA_OK
+    assert splitkv_status(mask=None, mask_planes=2) == fa.FA_ERR_INVALID_ARGUMENT
 
 
 def test_splitkv_empty_problem_is_a_no_op():

@@ -2,7 +2,7 @@
 
 Decode-shaped problems: one or a few query rows per sequence, every head of a GQA group in one
 32-row block, long and ragged key ranges cut into spans whose partial softmax states a second
-kernel merges.  Each case runs with the device's suggested number of spans and with a fixed
+kernel merges, with and without additive masks.  Each case runs with the device's suggested number of spans and with a fixed
 small and large one (spans past the key range hold no keys and must drop out of the merge).
 """
 
@@ -37,6 +37,18 @@ CASES = {
     "f16_d128_past_only_window": dict(seed=74, batch=2, heads=4, kv_heads=2, sq=1, sk=2048,
                                       dim=128, dtype="f16", causal=True, lengths="past_only",
                                       max_past=2047, local_window=40),
+    # additive masks: one plane per batch (float32, -inf holes), per head (input dtype, with
+    # softcap and fully masked rows), and a single plane with past lengths
+    "bf16_d128_mask_batch_planes": dict(seed=76, batch=2, heads=8, kv_heads=2, sq=1, sk=700,
+                                        dim=128, dtype="bf16", causal=True, mask="normal",
+                                        mask_p=0.2),
+    "f16_d64_mask_head_planes_softcap": dict(seed=77, batch=2, heads=4, kv_heads=2, sq=2, sk=500,
+                                             dim=64, dtype="f16", mask="bernoulli", mask_p=0.3,
+                                             mask_planes=8, mask_dtype="f16", softcap=20.0,
+                                             dead_rows=1),
+    "bf16_d128_mask_one_plane_past": dict(seed=78, batch=3, heads=16, kv_heads=2, sq=4, sk=600,
+                                          dim=128, dtype="bf16", causal=True, lengths="past",
+                                          max_past=590, mask="normal", mask_planes=1, dead_rows=1),
     # keys fewer than one tile, and total lengths of 0 (fully masked rows)
     "bf16_d128_short": dict(seed=75, batch=4, heads=4, kv_heads=1, sq=1, sk=20, dim=128,
                             dtype="bf16", lengths="total"),
@@ -44,9 +56,7 @@ CASES = {
 
 
 def _kwargs(prob):
-    kw = prob.to("cuda").kwargs()
-    kw.pop("mask")
-    return kw
+    return prob.to("cuda").kwargs()
 
 
 @pytest.mark.parametrize("splits", [None, 4, 64])

@@ -150,7 +150,7 @@ def splitkv_suggested_splits(batch: int, kv_heads: int, sk: int) -> int:
 
 
 def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
-                           sk: Optional[int] = None,
+                           sk: Optional[int] = None, mask: Optional[torch.Tensor] = None,
                            total_lengths: Optional[torch.Tensor] = None,
                            past_lengths: Optional[torch.Tensor] = None, causal: bool = False,
                            local_window: int = 0, scale: Optional[float] = None,
@@ -160,11 +160,12 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """The same attention forward with the keys split over workgroups (decode: few query rows).
 
-    Takes bf16/f16 inputs with head dim 64 or 128, (H / Hkv) * Sq <= 32 and no additive mask.
+    Takes bf16/f16 inputs with head dim 64 or 128 and (H / Hkv) * Sq <= 32; the mask as for
+    flash_attn_fwd.
     ``workspace`` (any dtype, contiguous, on q's device) needs splitkv_workspace_bytes(...) bytes;
     it is allocated here when None.
     """
-    args, out, stream = _marshal(q, k, v, sk, None, total_lengths, past_lengths, causal,
+    args, out, stream = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
                                  local_window, scale, softcap, out_layout, out, stream)
     B, _, _, D = q.shape
     Hkv, C = k.shape[1], k.shape[2]

@@ -274,8 +274,6 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
     if (st != FA_OK) return st;
     if (dtype == FA_DTYPE_F32 || (dim != 64 && dim != 128))
         return fail(FA_ERR_UNSUPPORTED, "the split-key path takes bf16/f16 inputs with head dim 64 or 128");
-    if (mask_planes != 0)
-        return fail(FA_ERR_UNSUPPORTED, "the split-key path takes no additive mask (use flash_attn_fwd)");
     if ((int64_t)(heads / kv_heads) * sq > 32)
         return fail(FA_ERR_UNSUPPORTED, "the split-key path needs (heads / kv_heads) * sq <= 32, got %lld",
                     (long long)(heads / kv_heads) * sq);
@@ -314,8 +312,8 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, s)
-                                                  : fa::launch_f16_splitkv(p, sp, dim, s);
+    const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, plan.maskk, s)
+                                                  : fa::launch_f16_splitkv(p, sp, dim, plan.maskk, s);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;
 }

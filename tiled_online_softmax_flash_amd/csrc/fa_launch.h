@@ -12,9 +12,9 @@ hipError_t launch_f16(const FwdParams& p, int dp, int grid, int maskk, bool soft
 hipError_t launch_f32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s);
 // fp32, head dims 129..384
 hipError_t launch_f32_wide(const FwdParams& p, int grid, bool masked, bool softcap, hipStream_t s);
-// split-key kernels (few query rows per KV head), head dims 64 and 128
-hipError_t launch_bf16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, hipStream_t s);
-hipError_t launch_f16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, hipStream_t s);
+// split-key kernels (few query rows per KV head), head dims 64 and 128; maskk as above
+hipError_t launch_bf16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, int maskk, hipStream_t s);
+hipError_t launch_f16_splitkv(const FwdParams& p, const SplitParams& sp, int dp, int maskk, hipStream_t s);
 // 256-row, 512-thread kernels for head dims 64 and 128 with 16-byte aligned rows.
 hipError_t launch_bf16_ring(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);
 hipError_t launch_f16_ring(const FwdParams& p, int dp, int grid, int maskk, bool softcap, hipStream_t s);

@@ -14,6 +14,8 @@
 //     unnormalised output in registers, which it writes to the workspace.  The kernel is bound
 //     by HBM bandwidth; its registers allow one wave per SIMD, so the grid is best at one
 //     workgroup per compute unit (fa_splitkv_suggested_splits).
+//   * An additive mask (one plane, one per batch or one per head) is read per lane, 16 keys of
+//     a tile at a time, and added after the optional softcap.
 //   * A second kernel merges the spans of every output row: with M the largest span maximum,
 //     O = sum_s 2^((m_s - M) k) O_s / sum_s 2^((m_s - M) k) l_s (0 when no span has a key).
 // LDS layouts, fragments and the softmax are those of the 256-row ring kernel (fa_fwd16_ring.h)
@@ -27,7 +29,8 @@ namespace fa {
 
 constexpr int kSplitThreads = 256;
 
-template <typename Tr, int DP, bool SOFTCAP, bool RAW>
+// MT: additive mask 0 none, 1 float32, 2 of the input type.
+template <typename Tr, int DP, bool SOFTCAP, bool RAW, int MT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kSplitThreads, kSplitThreads)))
 splitkv_kernel(const FwdParams p, const SplitParams sp) {
     using vec8 = typename Tr::vec8;
@@ -65,6 +68,14 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
     const int64_t hi = row_valid ? rule.hi(qi) : 0;
     const int my_lo32 = (int)(lo < 0x7fffffffLL ? lo : 0x7fffffffLL);
     const int my_hi32 = (int)(hi > -1 ? hi : -1);
+    // additive mask row of this query row (plane 0, b, or b * heads + h); read at clamped
+    // in-range key indices, keys past the row's range being removed by the key rule anyway
+    const char* mrow = nullptr;
+    if constexpr (MT != 0) {
+        const int64_t plane = mask_plane(p, b, hq);
+        const int64_t esz = MT == 1 ? 4 : 2;
+        mrow = (const char*)p.mask + ((plane * p.sq + qi) * (int64_t)p.sk) * esz;
+    }
     // keys any row of the block attends (lo and hi grow with the query row)
     const int64_t last_i = (sp.rows - 1) / p.group;
     const int64_t u_lo = rule.lo(0), u_hi = rule.hi(last_i);
@@ -138,6 +149,17 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
     auto compute = [&](int t, int slot) {
         const char* kt = lds + wave * WAVE_LDS + slot * SLOT;
         const char* vt = kt + HALF;
+        // mask values of this lane's 16 keys, requested before the tile's products
+        float mv[16];
+        if constexpr (MT != 0) {
+            const int kb = (t_begin + t) * 32 + 16 * hh;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int k = kb + v < p.sk ? kb + v : p.sk - 1;
+                if constexpr (MT == 1) mv[v] = row_valid ? ((const float*)mrow)[k] : 0.0f;
+                else mv[v] = row_valid ? (float)((const scalar*)mrow)[k] : 0.0f;
+            }
+        }
         f32x16 s = f32x16(0.0f);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -150,8 +172,15 @@ splitkv_kernel(const FwdParams p, const SplitParams sp) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             float x;
-            if constexpr (SOFTCAP) x = tanh_fast(s[v] * p.cap_y);
-            else x = RAW ? s[v] : s[v] * p.scale;
+            if constexpr (MT != 0) {
+                // natural units (kfac = log2 e): softcap first, then the mask
+                x = SOFTCAP ? __builtin_fmaf(p.softcap, tanh_fast(s[v] * p.cap_y), mv[v])
+                            : __builtin_fmaf(s[v], p.scale, mv[v]);
+            } else if constexpr (SOFTCAP) {
+                x = tanh_fast(s[v] * p.cap_y);
+            } else {
+                x = RAW ? s[v] : s[v] * p.scale;
+            }
             x = (v >= lo_rel && v <= hi_rel) ? x : neg_inf();
             s[v] = x;
             mt = __builtin_fmaxf(mt, x);
@@ -262,11 +291,11 @@ splitkv_merge_kernel(const FwdParams p, const SplitParams sp) {
     *(vec4s*)dst = __builtin_convertvector(acc * inv, vec4s);
 }
 
-template <typename Tr, int DP, bool SOFTCAP, bool RAW>
+template <typename Tr, int DP, bool SOFTCAP, bool RAW, int MT>
 hipError_t launch_splitkv_one(const FwdParams& p, const SplitParams& sp, hipStream_t s) {
     const int groups = p.batch * p.kv_heads;
-    hipLaunchKernelGGL((splitkv_kernel<Tr, DP, SOFTCAP, RAW>), dim3(groups * (sp.num_splits / 4)), dim3(kSplitThreads),
-                       0, s, p, sp);
+    hipLaunchKernelGGL((splitkv_kernel<Tr, DP, SOFTCAP, RAW, MT>), dim3(groups * (sp.num_splits / 4)),
+                       dim3(kSplitThreads), 0, s, p, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)p.batch * p.heads * p.sq * (DP / 4);
@@ -274,15 +303,22 @@ hipError_t launch_splitkv_one(const FwdParams& p, const SplitParams& sp, hipStre
     return hipGetLastError();
 }
 
-template <typename Tr>
-hipError_t launch_splitkv(const FwdParams& p, const SplitParams& sp, int dp, hipStream_t s) {
+template <typename Tr, int DP>
+hipError_t launch_splitkv_dp(const FwdParams& p, const SplitParams& sp, int maskk, hipStream_t s) {
     const bool cap = p.softcap > 0.0f;
-    if (dp == 64) return cap ? launch_splitkv_one<Tr, 64, true, false>(p, sp, s)
-                             : (p.raw_scores ? launch_splitkv_one<Tr, 64, false, true>(p, sp, s)
-                                             : launch_splitkv_one<Tr, 64, false, false>(p, sp, s));
-    return cap ? launch_splitkv_one<Tr, 128, true, false>(p, sp, s)
-               : (p.raw_scores ? launch_splitkv_one<Tr, 128, false, true>(p, sp, s)
-                               : launch_splitkv_one<Tr, 128, false, false>(p, sp, s));
+    if (maskk == 1) return cap ? launch_splitkv_one<Tr, DP, true, false, 1>(p, sp, s)
+                               : launch_splitkv_one<Tr, DP, false, false, 1>(p, sp, s);
+    if (maskk == 2) return cap ? launch_splitkv_one<Tr, DP, true, false, 2>(p, sp, s)
+                               : launch_splitkv_one<Tr, DP, false, false, 2>(p, sp, s);
+    if (cap) return launch_splitkv_one<Tr, DP, true, false, 0>(p, sp, s);
+    return p.raw_scores ? launch_splitkv_one<Tr, DP, false, true, 0>(p, sp, s)
+                        : launch_splitkv_one<Tr, DP, false, false, 0>(p, sp, s);
+}
+
+// maskk: 0 none, 1 float32 mask, 2 mask of the input type
+template <typename Tr>
+hipError_t launch_splitkv(const FwdParams& p, const SplitParams& sp, int dp, int maskk, hipStream_t s) {
+    return dp == 64 ? launch_splitkv_dp<Tr, 64>(p, sp, maskk, s) : launch_splitkv_dp<Tr, 128>(p, sp, maskk, s);
 }
 
 }  // namespace fa
