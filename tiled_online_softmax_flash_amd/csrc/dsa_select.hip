@@ -21,8 +21,6 @@
 //     go to the lower position).  The rest of the row is -1.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
 #include <hip/hip_runtime.h>
-#include <hip/hip_bf16.h>
-#include <hip/hip_fp16.h>
 
 #include <cstdint>
 
