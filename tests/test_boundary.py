@@ -243,3 +243,30 @@ def test_dsa_valid_arguments_pass():
 def test_dsa_invalid_arguments_are_rejected(over, code):
     assert dsa_status(**over) == code, fa.last_error()
     assert fa.last_error() != ""
+
+
+def test_new_bindings_reject_host_tensors():
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 32, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd_splitkv(q, k, k)
+    with pytest.raises(ValueError):
+        fa.dsa_index_select(torch.zeros(1, 1, 2, 8), torch.zeros(1, 5, 8), torch.zeros(1, 1, 2),
+                            torch.zeros(1, 1, 1, 5), top_k=2, scale=1.0)
+
+
+def test_dsa_binding_checks_shapes_and_dtypes():
+    q, k, w, b = torch.zeros(1, 1, 2, 8), torch.zeros(1, 5, 8), torch.zeros(1, 1, 2), torch.zeros(1, 1, 1, 5)
+    with pytest.raises(ValueError):
+        fa.dsa_index_select(q, torch.zeros(1, 5, 4), w, b, top_k=2, scale=1.0)      # head dim
+    with pytest.raises(ValueError):
+        fa.dsa_index_select(q, k, w, b.double(), top_k=2, scale=1.0)               # bias dtype
+    with pytest.raises(ValueError):
+        fa.dsa_index_select(q, k.half(), w, b, top_k=2, scale=1.0)                 # mixed dtypes
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    import bench
+
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
