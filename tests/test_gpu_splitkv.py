@@ -49,6 +49,11 @@ CASES = {
     "bf16_d128_mask_one_plane_past": dict(seed=78, batch=3, heads=16, kv_heads=2, sq=4, sk=600,
                                           dim=128, dtype="bf16", causal=True, lengths="past",
                                           max_past=590, mask="normal", mask_planes=1, dead_rows=1),
+    # token-major output with a bf16 mask per head and a window
+    "bf16_d64_token_major_head_mask": dict(seed=79, batch=2, heads=6, kv_heads=3, sq=3, sk=450,
+                                           dim=64, dtype="bf16", out_layout="token", causal=True,
+                                           local_window=200, mask="normal", mask_planes=12,
+                                           mask_dtype="bf16", dead_rows=1),
     # keys fewer than one tile, and total lengths of 0 (fully masked rows)
     "bf16_d128_short": dict(seed=75, batch=4, heads=4, kv_heads=1, sq=1, sk=20, dim=128,
                             dtype="bf16", lengths="total"),
