@@ -62,6 +62,27 @@ def traffic_from_profile(workload: str):
     return rec.get("traffic_bytes")
 
 
+def warm_up(step, count: int, min_seconds: float) -> float:
+    """Runs ``count`` untimed steps, then keeps running steps until at least ``min_seconds`` of
+    wall time have passed since the first one; returns the seconds spent.
+
+    The GPU's clocks ramp up over the first few tenths of a second of sustained load (from idle,
+    the first launches of the GQA causal workload run 15-30 % slower), so a warm-up given only
+    as a step count can leave a short timed region measuring the ramp instead of the kernel."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(count):
+        step()
+    torch.cuda.synchronize()
+    batch = 8
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        batch = min(batch * 2, 256)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(prob, out_gpu: torch.Tensor, target_s: float):
     """The oracle as it stands, timed on a bounded row sample of the same workload."""
     import oracle
@@ -129,9 +150,7 @@ def bench_dsa(args) -> int:
     def step():
         fa.dsa_index_select(d.query, d.key, d.weights, d.bias, out=out, workspace=ws, **prob.kwargs())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_s = warm_up(step, args.warmup, args.clock_warmup)
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -150,6 +169,7 @@ def bench_dsa(args) -> int:
         "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3),
         "unit": "Tops/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": prob.dtype,
@@ -201,9 +221,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU ramps its clocks over the first ~0.1-0.3 s of sustained load: the default warmup
-    # (about 0.35 s of the GQA causal workload) lets the timed steps see the steady state
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=10)
+    # untimed steps continue after --warmup until this much wall time has passed: the GPU ramps
+    # its clocks over the first ~0.1-0.3 s of sustained load, whatever the step count
+    ap.add_argument("--clock-warmup", type=float, default=1.0, metavar="SECONDS")
     ap.add_argument("--workload", default="gqa_causal",
                     choices=list(workloads.WORKLOADS) + list(workloads.DSA_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -281,9 +302,7 @@ def main(argv=None) -> int:
         def step():
             fa.flash_attn_fwd(dev.q, dev.k, dev.v, out=out, **kw)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_s = warm_up(step, args.warmup, args.clock_warmup)
 
     # one event pair around the whole timed region: per-launch event pairs would add their own
     # marker packets between the kernels
@@ -316,6 +335,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

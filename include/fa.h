@@ -20,6 +20,11 @@
  *   plane = 0 when mask_planes == 1, b when mask_planes == batch, b*heads + h when
  *   mask_planes == batch*heads (checked in that order).
  *
+ *   Reading of total_lengths[b] > sk: the page's kernels never score a key at or past sk, so
+ *   L is capped at sk; without past_lengths the causal base is that capped L (L - sq + i),
+ *   whereas the page's kernel body subtracts sq from the uncapped total.  The two agree
+ *   whenever total_lengths[b] <= sk.
+ *
  * Threading and ownership: every pointer is caller-owned DEVICE memory, dense and contiguous
  * in the layout stated per argument; the library never allocates, frees, copies to the host
  * or synchronises on the call path and keeps no state between calls except the thread-local
@@ -100,6 +105,12 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
  * fa_check_args — the argument validation flash_attn_fwd performs, without enqueuing
  * anything or touching the HIP runtime.  Same arguments (minus the stream), same status
  * codes.  Pointers are only checked for NULL where they are required.
+ *
+ * This is the claim-time gate of the flash_attention.rs page: its `supported` function (which
+ * accepts head dims 1..128 and routes single-query calls elsewhere) and the checks `run` makes
+ * before it launches (dtype dispatch, checked narrowing of sizes to the kernel's integer
+ * types, grid overflow).  Here the head-dim range is 1..128 for 16-bit inputs and 1..384 for
+ * FA_DTYPE_F32, sq == 1 is accepted, and the layout sizes are checked as well.
  */
 int fa_check_args(const void* q, const void* k, const void* v, const void* mask,
                   const int32_t* total_lengths, const int32_t* past_lengths, const void* out,
@@ -149,7 +160,13 @@ size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_spli
 int fa_splitkv_suggested_splits(int batch, int kv_heads, int sk);
 
 /* Thread-local text describing the most recent non-FA_OK status on this thread ("" if none).
- * The pointer stays valid until the next call into the library on the same thread. */
+ * The pointer stays valid until the next call into the library on the same thread.
+ *
+ * The flash_attention.rs page's host function `run` reports failures as typed errors carrying
+ * a message: "not implemented" for shapes and dtypes outside the kernels (FA_ERR_UNSUPPORTED
+ * here), and a kernel failure for sizes that do not narrow to the kernel's integer types and
+ * for a failed launch (FA_ERR_OVERFLOW and FA_ERR_HIP here).  A C ABI returns the status as an
+ * integer and keeps the message here. */
 const char* fa_last_error(void);
 
 /* Library version, e.g. "0.1.0". */

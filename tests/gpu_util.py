@@ -89,3 +89,43 @@ def sample_rows(prob, n: int, seed: int = 1234, extra=()) -> list:
     while len(rows) < target:
         rows.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq))))
     return sorted(rows)
+
+
+def busy_stream(seconds_hint: int = 30) -> torch.cuda.Stream:
+    """A new stream held busy by a chain of fp32 matrix products (tens of milliseconds), after
+    waiting for the current stream's work (the inputs' copies)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        a = torch.full((2048, 2048), 1e-3, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(seconds_hint):
+            torch.mm(a, a, out=b)
+            torch.mm(b, b, out=a)
+    return side
+
+
+class AllocSpy:
+    """Records the tensors torch.empty returns while installed (monkeypatched by a test)."""
+
+    def __init__(self):
+        self.ptrs = set()
+        self._real = torch.empty
+
+    def __call__(self, *args, **kwargs):
+        t = self._real(*args, **kwargs)
+        if t.is_cuda and t.numel():
+            self.ptrs.add(t.data_ptr())
+        return t
+
+
+def churn_hits(ptrs, nbytes: int, rounds: int = 64) -> int:
+    """Allocates and fills ``rounds`` byte tensors of ``nbytes`` on the current stream; returns how
+    many of them landed on an address in ``ptrs``."""
+    hits = 0
+    for _ in range(rounds):
+        y = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        hits += int(y.data_ptr() in ptrs)
+        y.fill_(0xFF)
+        del y
+    return hits

@@ -1,8 +1,11 @@
 """Each plausible mistake planted in a copy of the index-selection oracle must make at least one
 of its pins (tests/test_dsa_oracle_pins.py) fail.  Copies are built with gcc in a temporary
-directory and checked in a child pytest process.  CPU only."""
+directory and checked in a child pytest process.  A mutant counts as caught when that run ends
+with failed pins, or when the child is ended by a signal; a collection or usage error is a
+failure of the harness.  CPU only."""
 
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -47,4 +50,11 @@ def test_mutant_is_caught(name, old, new, tmp_path):
     proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", "test_dsa_oracle_pins.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    if proc.returncode < 0:
+        return  # the planted mistake crashed the oracle (the child ended by a signal): caught
+    # pytest exits with 1 when tests ran and some failed; 2-5 mean an interrupted run, an
+    # internal or usage error, or no tests collected: failures of the harness, not catches
     assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
+    assert proc.returncode == 1 and re.search(r"\b\d+ failed\b", proc.stdout), (
+        f"the pin run for mutant {name} did not end in failed pins (exit {proc.returncode}):\n"
+        f"{proc.stdout[-2000:]}{proc.stderr[-2000:]}")

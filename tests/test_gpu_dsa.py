@@ -177,3 +177,26 @@ def test_dsa_on_a_side_stream():
     side.synchronize()
     want = dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs())
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_dsa_side_stream_not_current_keeps_workspace(monkeypatch):
+    """stream= names a stream that is not the current one: the workspace the binding allocates
+    must not be handed to work on the current stream before the side stream's kernels ran."""
+    from gpu_util import AllocSpy, busy_stream, churn_hits
+
+    prob = workloads.make_dsa_problem(name="side2", **CASES["bf16_decode_d128"])
+    d = prob.to("cuda")
+    B, S, _, _ = prob.query.shape
+    need = fa.dsa_workspace_bytes(B, S, prob.key.shape[1])
+    side = busy_stream()
+    spy = AllocSpy()
+    say("[gpu] dsa on a side stream that is not current, allocations churned meanwhile")
+    monkeypatch.setattr(torch, "empty", spy)
+    out = fa.dsa_index_select(d.query, d.key, d.weights, d.bias, stream=side, **prob.kwargs())
+    monkeypatch.undo()
+    assert spy.ptrs, "the binding allocated nothing"
+    hits = churn_hits(spy.ptrs - {out.data_ptr()}, need)
+    side.synchronize()
+    assert hits == 0, "the workspace was reused while the side stream still needed it"
+    want = dsa_oracle.index_select(prob.query, prob.key, prob.weights, prob.bias, **prob.kwargs())
+    assert np.array_equal(out.cpu().numpy(), want)

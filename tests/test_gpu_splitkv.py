@@ -147,3 +147,26 @@ def test_splitkv_on_a_side_stream():
         out = fa.flash_attn_fwd_splitkv(d.q, d.k, d.v, num_splits=8, stream=side, **kw)
     side.synchronize()
     check(out.double().cpu().numpy(), oracle_full(prob), prob.dtype, "side-stream")
+
+
+def test_splitkv_side_stream_not_current_keeps_workspace(monkeypatch):
+    """stream= names a stream that is not the current one: the workspace the binding allocates
+    must not be handed to work on the current stream before the side stream's kernels ran."""
+    from gpu_util import AllocSpy, busy_stream, churn_hits
+
+    prob = workloads.make_problem(name="side2", **CASES["bf16_d128_decode_total"])
+    d = prob.to("cuda")
+    kw = d.kwargs()
+    splits = 8
+    need = fa.splitkv_workspace_bytes(prob.batch, prob.kv_heads, prob.dim, splits)
+    side = busy_stream()
+    spy = AllocSpy()
+    say("[gpu] splitkv on a side stream that is not current, allocations churned meanwhile")
+    monkeypatch.setattr(torch, "empty", spy)
+    out = fa.flash_attn_fwd_splitkv(d.q, d.k, d.v, num_splits=splits, stream=side, **kw)
+    monkeypatch.undo()
+    assert spy.ptrs, "the binding allocated nothing"
+    hits = churn_hits(spy.ptrs - {out.data_ptr()}, need)
+    side.synchronize()
+    assert hits == 0, "the workspace was reused while the side stream still needed it"
+    check(out.double().cpu().numpy(), oracle_full(prob), prob.dtype, "side-stream-not-current")

@@ -1,7 +1,9 @@
 """Each plausible mistake planted in a copy of the oracle must be caught by at least one pin.
 
 The copies are built with gcc into a temporary directory and exercised in a child process (a
-planted mistake may read out of bounds; a crash then only ends the child).  CPU only.
+planted mistake may read out of bounds; a crash then only ends the child).  A mutant counts as
+caught when the child names at least one failed pin, or when it is ended by a signal; any other
+failure of the child is a failure of the harness.  CPU only.
 """
 
 import json
@@ -50,6 +52,11 @@ MUTANTS = [
      "const float* qrow = p->q + ((b * p->heads + kvh) * p->sq + i) * D;"),
     ("values_from_keys", "o[d] += w * (double)vbase[j * D + d];",
      "o[d] += w * (double)kbase[j * D + d];"),
+    # the causal base from the uncapped total length (the other reading of total > sk)
+    ("causal_base_uncapped_total", ": L - p->sq + i;",
+     ": (p->total_lengths != NULL ? (int64_t)p->total_lengths[b] : p->sk) - p->sq + i;"),
+    ("total_not_capped_at_sk", "(int64_t)p->total_lengths[b] < L) L = p->total_lengths[b];",
+     "(int64_t)p->total_lengths[b] != L) L = p->total_lengths[b];"),
 ]
 
 _DRIVER = r"""
@@ -87,8 +94,11 @@ def test_planted_mistake_is_caught(source, name, old, new, tmp_path):
     driver = _DRIVER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
     proc = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True,
                           timeout=300)
-    if proc.returncode != 0:
-        return  # the planted mistake crashed the oracle: caught
+    if proc.returncode < 0:
+        return  # the planted mistake crashed the oracle (the child ended by a signal): caught
+    # anything else must be a clean run of the driver that names the failed pins; an import
+    # error or another failure of the harness itself is not a catch
+    assert proc.returncode == 0, f"the pin driver failed for {name}:\n{proc.stdout}{proc.stderr}"
     line = [ln for ln in proc.stdout.splitlines() if ln.startswith("FAILED_PINS=")]
     assert line, proc.stdout + proc.stderr
     failed = json.loads(line[-1].split("=", 1)[1])

@@ -130,12 +130,13 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sk: Opt
     mask [planes,Sq,Sk] (fp32 or q's dtype); total/past lengths int32 [B] on the device.
     Returns out [B,H,Sq,D] (``out_layout="head"``) or [B,Sq,H*D] (``"token"``).
     """
-    args, out, stream = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
-                                 local_window, scale, softcap, out_layout, out, stream)
+    args, out, stream, made = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
+                                       local_window, scale, softcap, out_layout, out, stream)
     lib = _load()
     status = lib.flash_attn_fwd(*args, stream.cuda_stream)
     if status != FA_OK:
         raise FaError(status, lib.fa_last_error().decode())
+    _keep_until_done(stream, *made)
     return out
 
 
@@ -165,8 +166,8 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     ``workspace`` (any dtype, contiguous, on q's device) needs splitkv_workspace_bytes(...) bytes;
     it is allocated here when None.
     """
-    args, out, stream = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
-                                 local_window, scale, softcap, out_layout, out, stream)
+    args, out, stream, made = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
+                                       local_window, scale, softcap, out_layout, out, stream)
     B, _, _, D = q.shape
     Hkv, C = k.shape[1], k.shape[2]
     if num_splits is None:
@@ -174,6 +175,7 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     need = splitkv_workspace_bytes(B, Hkv, D, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        made = made + (workspace,)
     elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
         raise ValueError("workspace must be a contiguous tensor on q's device")
     lib = _load()
@@ -181,6 +183,7 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if status != FA_OK:
         raise FaError(status, lib.fa_last_error().decode())
+    _keep_until_done(stream, *made)
     return out
 
 
@@ -218,8 +221,10 @@ def dsa_index_select(query: torch.Tensor, key: torch.Tensor, weights: torch.Tens
         raise ValueError("query, key and weights must share one dtype among float32, float16, bfloat16")
     if bias.dtype != torch.float32:
         raise ValueError("bias must be float32")
+    made = ()
     if out is None:
         out = torch.empty((B, 1, S, int(top_k)), dtype=torch.int64, device=query.device)
+        made = (out,)
     elif out.dtype != torch.int64 or tuple(out.shape) != (B, 1, S, int(top_k)):
         raise ValueError(f"out must be int64 [B, 1, S, top_k], got {out.dtype} {tuple(out.shape)}")
     for t in (query, key, weights, bias, out):
@@ -228,6 +233,7 @@ def dsa_index_select(query: torch.Tensor, key: torch.Tensor, weights: torch.Tens
     need = dsa_workspace_bytes(B, S, T)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+        made = made + (workspace,)
     elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != query.device:
         raise ValueError("workspace must be a contiguous tensor on query's device")
     if stream is None:
@@ -240,12 +246,23 @@ def dsa_index_select(query: torch.Tensor, key: torch.Tensor, weights: torch.Tens
                                   stream.cuda_stream)
     if status != FA_OK:
         raise FaError(status, lib.fa_last_error().decode())
+    _keep_until_done(stream, *made)
     return out
+
+
+def _keep_until_done(stream, *tensors) -> None:
+    """Tensors allocated here come from torch's caching allocator on the current stream, while
+    the kernels run on ``stream``.  Recording ``stream`` on them keeps the allocator from handing
+    their memory to other work before the kernels enqueued there have finished (the caller may
+    drop the workspace at once, or the output before synchronising)."""
+    for t in tensors:
+        t.record_stream(stream)
 
 
 def _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal, local_window, scale,
              softcap, out_layout, out, stream):
-    """Checks the tensors and returns the C argument list (without the stream), out, stream."""
+    """Checks the tensors; returns the C argument list (without the stream), out, the stream and
+    the tuple of tensors allocated here."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,Hkv,C,D]")
     B, H, Sq, D = q.shape
@@ -277,9 +294,11 @@ def _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal, local_windo
         if t is not None and (t.dtype != torch.int32 or t.shape != (B,)):
             raise ValueError(f"{name} must be int32 [B]")
     layout = _LAYOUT_CODE[out_layout]
+    made = ()
     if out is None:
         shape = (B, H, Sq, D) if layout == 0 else (B, Sq, H * D)
         out = torch.empty(shape, dtype=q.dtype, device=q.device)
+        made = (out,)
     elif out.dtype != q.dtype or out.numel() != B * H * Sq * D:
         raise ValueError("out must match q's dtype and element count")
     if scale is None:
@@ -289,4 +308,4 @@ def _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal, local_windo
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(total_lengths), _ptr(past_lengths), _ptr(out),
             B, H, Hkv, Sq, sk, C, D, 1 if causal else 0, planes, int(local_window), float(scale),
             float(softcap), _DTYPE_CODE[q.dtype], mask_dtype, layout]
-    return args, out, stream
+    return args, out, stream, made
