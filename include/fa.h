@@ -150,6 +150,37 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
                            float softcap, int dtype, int mask_dtype, int out_layout,
                            int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the static device scratch of flash_attn_fwd_splitkv_noalloc (16 MiB per device). */
+#define FA_SPLITKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * flash_attn_fwd_splitkv_noalloc — flash_attn_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments minus the workspace, same kernels, same result (bit for bit, at
+ * the same num_splits).  The spans' partial states go to a static device array of
+ * FA_SPLITKV_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on until the
+ * process ends; nothing is allocated, freed or cleared per call.
+ *
+ *   Limit:    fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits) must not exceed
+ *             FA_SPLITKV_NOALLOC_SCRATCH_BYTES; larger calls return FA_ERR_UNSUPPORTED (use
+ *             fewer spans, or flash_attn_fwd_splitkv with a workspace).
+ *   Sharing:  every call on one device uses the same scratch, which keeps the last call's
+ *             contents.  Calls whose work overlaps in time on one device (two streams, two
+ *             host threads) race on it and give wrong results: serialise them, e.g. on one
+ *             stream.  Nothing in the scratch needs to start at zero: every span writes its
+ *             state before the merge reads it.
+ *   Set-up:   the first call on each device looks up the scratch's device address once
+ *             (hipGetSymbolAddress; no stream work) and caches it; make that first call
+ *             outside graph capture.  FA_ERR_HIP if the lookup fails.
+ *   Other errors: those of flash_attn_fwd_splitkv except the workspace checks.
+ */
+int flash_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, const void* mask,
+                                   const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                                   int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity,
+                                   int dim, int causal, int mask_planes, int local_window, float scale,
+                                   float softcap, int dtype, int mask_dtype, int out_layout, int num_splits,
+                                   void* stream);
+
 /* Workspace bytes flash_attn_fwd_splitkv needs: num_splits * batch * kv_heads * 32 rows of
  * (dim + 2) floats.  0 for invalid arguments or on overflow.  Host only. */
 size_t fa_splitkv_workspace_bytes(int batch, int kv_heads, int dim, int num_splits);

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_check_args", "fa_last_error", "fa_splitkv_suggested_splits",
                                     "fa_splitkv_workspace_bytes", "fa_version", "flash_attn_fwd",
-                                    "flash_attn_fwd_splitkv"]
+                                    "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -167,6 +167,39 @@ def test_splitkv_takes_masks():
 
 def test_splitkv_empty_problem_is_a_no_op():
     assert splitkv_status(sq=0) == fa.FA_OK
+
+
+def noalloc_status(num_splits=8, **over):
+    """flash_attn_fwd_splitkv_noalloc's status for fake device pointers."""
+    args = dict(GOOD, sq=1, heads=8, kv_heads=2, dim=128)
+    args.update(over)
+    fa._load()
+    f = fa._lib.flash_attn_fwd_splitkv_noalloc
+    return f(args["q"], args["k"], args["v"], args.get("mask"), None, None, args["out"], args["batch"],
+             args["heads"], args["kv_heads"], args["sq"], args["sk"], args["kv_capacity"], args["dim"],
+             args["causal"], args["mask_planes"], args["local_window"], args["scale"], args["softcap"],
+             args["dtype"], args["mask_dtype"], args["out_layout"], num_splits, None)
+
+
+def test_noalloc_checks_before_touching_the_device():
+    # every check of the workspace entry point except the workspace's own, then the scratch limit;
+    # all of them return before the scratch's address is looked up
+    assert noalloc_status(sq=0) == fa.FA_OK
+    assert noalloc_status(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc_status(num_splits=6) == fa.FA_ERR_INVALID_ARGUMENT
+    assert noalloc_status(heads=6, kv_heads=4) == fa.FA_ERR_INVALID_ARGUMENT
+    # 64 batch x 8 KV heads x 64 spans x 32 rows x 130 floats = 545 MB > the 16 MiB scratch
+    need = fa.splitkv_workspace_bytes(64, 8, 128, 64)
+    assert need > fa.SPLITKV_NOALLOC_SCRATCH_BYTES
+    assert noalloc_status(batch=64, heads=32, kv_heads=8, sk=4096, kv_capacity=4096,
+                          num_splits=64) == fa.FA_ERR_UNSUPPORTED
+    assert "static scratch" in fa.last_error()
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_SPLITKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.SPLITKV_NOALLOC_SCRATCH_BYTES
 
 
 # ---- sparse index selection (include/dsa.h)

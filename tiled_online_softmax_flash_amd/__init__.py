@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "flash_attn_fwd", "flash_attn_fwd_splitkv", "splitkv_workspace_bytes", "splitkv_suggested_splits",
+    "flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_noalloc",
+    "splitkv_workspace_bytes", "splitkv_suggested_splits", "SPLITKV_NOALLOC_SCRATCH_BYTES",
     "check_args", "last_error", "version", "FaError", "library_path",
     "FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED", "FA_ERR_OVERFLOW", "FA_ERR_HIP",
     "FA_DTYPE_F32", "FA_DTYPE_F16", "FA_DTYPE_BF16",
@@ -31,6 +32,9 @@ FA_ERR_HIP = -4
 FA_DTYPE_F32 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_BF16 = 2
+
+# the static device scratch of flash_attn_fwd_splitkv_noalloc (FA_SPLITKV_NOALLOC_SCRATCH_BYTES)
+SPLITKV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _DTYPE_CODE = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
                torch.bfloat16: FA_DTYPE_BF16}
@@ -73,6 +77,8 @@ def _load():
         lib.flash_attn_fwd_splitkv.argtypes = _ARGS + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                        ctypes.c_void_p]
         lib.flash_attn_fwd_splitkv.restype = ctypes.c_int
+        lib.flash_attn_fwd_splitkv_noalloc.argtypes = _ARGS + [ctypes.c_int, ctypes.c_void_p]
+        lib.flash_attn_fwd_splitkv_noalloc.restype = ctypes.c_int
         lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 4
         lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_splitkv_suggested_splits.argtypes = [ctypes.c_int] * 3
@@ -181,6 +187,33 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     lib = _load()
     status = lib.flash_attn_fwd_splitkv(*args, int(num_splits), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if status != FA_OK:
+        raise FaError(status, lib.fa_last_error().decode())
+    _keep_until_done(stream, *made)
+    return out
+
+
+def flash_attn_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                                   sk: Optional[int] = None, mask: Optional[torch.Tensor] = None,
+                                   total_lengths: Optional[torch.Tensor] = None,
+                                   past_lengths: Optional[torch.Tensor] = None,
+                                   causal: bool = False, local_window: int = 0,
+                                   scale: Optional[float] = None, softcap: float = 0.0,
+                                   out_layout: str = "head", out: Optional[torch.Tensor] = None,
+                                   num_splits: Optional[int] = None,
+                                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """flash_attn_fwd_splitkv without a workspace: the library keeps the spans' partial states in
+    a static device scratch of SPLITKV_NOALLOC_SCRATCH_BYTES (the C entry point allocates
+    nothing).  Calls that overlap in time on one device race on that scratch.  Pass ``out`` to
+    keep this call free of allocations on the Python side too."""
+    args, out, stream, made = _marshal(q, k, v, sk, mask, total_lengths, past_lengths, causal,
+                                       local_window, scale, softcap, out_layout, out, stream)
+    B, _, _, _ = q.shape
+    Hkv, C = k.shape[1], k.shape[2]
+    if num_splits is None:
+        num_splits = splitkv_suggested_splits(B, Hkv, C if sk is None else int(sk))
+    lib = _load()
+    status = lib.flash_attn_fwd_splitkv_noalloc(*args, int(num_splits), stream.cuda_stream)
     if status != FA_OK:
         raise FaError(status, lib.fa_last_error().decode())
     _keep_until_done(stream, *made)

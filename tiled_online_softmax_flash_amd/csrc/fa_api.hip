@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "../../include/fa.h"
@@ -186,6 +187,104 @@ int device_cu_count() {
     return n;
 }
 
+// Scratch for flash_attn_fwd_splitkv_noalloc: the split-key spans' partial states, for callers
+// that cannot allocate.  One copy per device, held until the process ends; every call on a
+// device shares it (calls that overlap in time on one device race on it).  Host code never
+// passes this name to a kernel: on the host it is only a stand-in for the symbol, and the
+// device address comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) char scratch[FA_SPLITKV_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device and cached.
+// Returns nullptr (with the error text set) when the lookup fails.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        fail(FA_ERR_HIP, "cannot determine the current device for the static scratch");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            fail(FA_ERR_HIP, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        cache[dev] = ptr;
+    }
+    return cache[dev];
+}
+
+// flash_attn_fwd_splitkv with a caller workspace, or (static_scratch) with the static scratch.
+int splitkv_run(const void* q, const void* k, const void* v, const void* mask,
+                const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity, int dim,
+                int causal, int mask_planes, int local_window, float scale, float softcap,
+                int dtype, int mask_dtype, int out_layout, int num_splits, void* workspace,
+                size_t workspace_bytes, bool static_scratch, void* stream) {
+    Plan plan;
+    const int st = validate(q, k, v, mask, out, batch, heads, kv_heads, sq, sk, kv_capacity, dim,
+                            mask_planes, scale, softcap, dtype, mask_dtype, out_layout, &plan);
+    if (st != FA_OK) return st;
+    if (dtype == FA_DTYPE_F32 || (dim != 64 && dim != 128))
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path takes bf16/f16 inputs with head dim 64 or 128");
+    if ((int64_t)(heads / kv_heads) * sq > 32)
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs (heads / kv_heads) * sq <= 32, got %lld",
+                    (long long)(heads / kv_heads) * sq);
+    if (!aligned(q, 16) || !aligned(out, 16) || (sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs 16-byte aligned q, k, v and out");
+    if ((int64_t)kv_capacity * dim * 2 >= 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "a (batch, KV head) cache of %lld bytes exceeds the 2 GiB the split-key "
+                    "path addresses", (long long)kv_capacity * dim * 2);
+    if (num_splits < 4 || num_splits % 4 != 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be a positive multiple of 4, got %d", num_splits);
+    if (plan.empty) return FA_OK;
+    const size_t need = fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits);
+    if (need == 0) return fail(FA_ERR_OVERFLOW, "the split-key workspace size overflows");
+    if (static_scratch) {
+        if (need > (size_t)FA_SPLITKV_NOALLOC_SCRATCH_BYTES)
+            return fail(FA_ERR_UNSUPPORTED, "the split-key state of this call needs %zu bytes, more than the "
+                        "%zu-byte static scratch of flash_attn_fwd_splitkv_noalloc (use fewer spans, or "
+                        "flash_attn_fwd_splitkv with a workspace)", need,
+                        (size_t)FA_SPLITKV_NOALLOC_SCRATCH_BYTES);
+        workspace = scratch_address();
+        if (workspace == nullptr) return FA_ERR_HIP;
+        workspace_bytes = FA_SPLITKV_NOALLOC_SCRATCH_BYTES;
+    }
+    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARGUMENT, "the split-key path needs a 16-byte aligned workspace of %zu bytes "
+                    "(got %zu at %p)", need, workspace_bytes, workspace);
+    int64_t grid1;
+    if (!mul_ok((int64_t)batch * kv_heads, num_splits / 4, &grid1) || grid1 > 0x7fffffffLL)
+        return fail(FA_ERR_OVERFLOW, "split-key grid exceeds the launch limit");
+
+    fa::FwdParams& p = plan.p;
+    p.total_lengths = total_lengths;
+    p.past_lengths = past_lengths;
+    p.causal = causal != 0;
+    p.window = local_window > 0 ? local_window : 0;
+    fa::SplitParams sp;
+    const int64_t ws_rows = (int64_t)num_splits * batch * kv_heads * 32;
+    sp.ws_o = (float*)workspace;
+    sp.ws_m = sp.ws_o + ws_rows * dim;
+    sp.ws_l = sp.ws_m + ws_rows;
+    sp.num_splits = num_splits;
+    const int64_t tiles = ((int64_t)sk + 31) / 32;
+    sp.span = (int)(((tiles + num_splits - 1) / num_splits) * 32);
+    if (sp.span < 32) sp.span = 32;
+    sp.rows = (heads / kv_heads) * sq;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, plan.maskk, s)
+                                                  : fa::launch_f16_splitkv(p, sp, dim, plan.maskk, s);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,54 +367,20 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, const vo
                            int causal, int mask_planes, int local_window, float scale, float softcap,
                            int dtype, int mask_dtype, int out_layout, int num_splits, void* workspace,
                            size_t workspace_bytes, void* stream) {
-    Plan plan;
-    const int st = validate(q, k, v, mask, out, batch, heads, kv_heads, sq, sk, kv_capacity, dim,
-                            mask_planes, scale, softcap, dtype, mask_dtype, out_layout, &plan);
-    if (st != FA_OK) return st;
-    if (dtype == FA_DTYPE_F32 || (dim != 64 && dim != 128))
-        return fail(FA_ERR_UNSUPPORTED, "the split-key path takes bf16/f16 inputs with head dim 64 or 128");
-    if ((int64_t)(heads / kv_heads) * sq > 32)
-        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs (heads / kv_heads) * sq <= 32, got %lld",
-                    (long long)(heads / kv_heads) * sq);
-    if (!aligned(q, 16) || !aligned(out, 16) || (sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
-        return fail(FA_ERR_UNSUPPORTED, "the split-key path needs 16-byte aligned q, k, v and out");
-    if ((int64_t)kv_capacity * dim * 2 >= 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "a (batch, KV head) cache of %lld bytes exceeds the 2 GiB the split-key "
-                    "path addresses", (long long)kv_capacity * dim * 2);
-    if (num_splits < 4 || num_splits % 4 != 0)
-        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be a positive multiple of 4, got %d", num_splits);
-    if (plan.empty) return FA_OK;
-    const size_t need = fa_splitkv_workspace_bytes(batch, kv_heads, dim, num_splits);
-    if (need == 0) return fail(FA_ERR_OVERFLOW, "the split-key workspace size overflows");
-    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
-        return fail(FA_ERR_INVALID_ARGUMENT, "the split-key path needs a 16-byte aligned workspace of %zu bytes "
-                    "(got %zu at %p)", need, workspace_bytes, workspace);
-    int64_t grid1;
-    if (!mul_ok((int64_t)batch * kv_heads, num_splits / 4, &grid1) || grid1 > 0x7fffffffLL)
-        return fail(FA_ERR_OVERFLOW, "split-key grid exceeds the launch limit");
+    return splitkv_run(q, k, v, mask, total_lengths, past_lengths, out, batch, heads, kv_heads, sq, sk,
+                       kv_capacity, dim, causal, mask_planes, local_window, scale, softcap, dtype, mask_dtype,
+                       out_layout, num_splits, workspace, workspace_bytes, false, stream);
+}
 
-    fa::FwdParams& p = plan.p;
-    p.total_lengths = total_lengths;
-    p.past_lengths = past_lengths;
-    p.causal = causal != 0;
-    p.window = local_window > 0 ? local_window : 0;
-    fa::SplitParams sp;
-    const int64_t ws_rows = (int64_t)num_splits * batch * kv_heads * 32;
-    sp.ws_o = (float*)workspace;
-    sp.ws_m = sp.ws_o + ws_rows * dim;
-    sp.ws_l = sp.ws_m + ws_rows;
-    sp.num_splits = num_splits;
-    const int64_t tiles = ((int64_t)sk + 31) / 32;
-    sp.span = (int)(((tiles + num_splits - 1) / num_splits) * 32);
-    if (sp.span < 32) sp.span = 32;
-    sp.rows = (heads / kv_heads) * sq;
-
-    hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();
-    const hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bf16_splitkv(p, sp, dim, plan.maskk, s)
-                                                  : fa::launch_f16_splitkv(p, sp, dim, plan.maskk, s);
-    if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
-    return FA_OK;
+int flash_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, const void* mask,
+                                   const int32_t* total_lengths, const int32_t* past_lengths, void* out,
+                                   int batch, int heads, int kv_heads, int sq, int sk, int kv_capacity,
+                                   int dim, int causal, int mask_planes, int local_window, float scale,
+                                   float softcap, int dtype, int mask_dtype, int out_layout, int num_splits,
+                                   void* stream) {
+    return splitkv_run(q, k, v, mask, total_lengths, past_lengths, out, batch, heads, kv_heads, sq, sk,
+                       kv_capacity, dim, causal, mask_planes, local_window, scale, softcap, dtype, mask_dtype,
+                       out_layout, num_splits, nullptr, 0, true, stream);
 }
 
 size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq) {
