@@ -12,7 +12,7 @@ import torch
 
 import tiled_online_softmax_flash_amd as fa
 import workloads
-from gpu_util import (TOL, check, gpu_rows, oracle_full, oracle_rows, run_gpu, sample_rows, say)
+from gpu_util import TOL, check, oracle_full, run_gpu, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -35,23 +35,23 @@ def test_small_workload_full_output(name):
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_full_workload_sampled_rows(name):
+def test_full_workload_full_output(name):
+    """The whole output at full size, in the launch configuration bench.py times (the split-key
+    entry point for the decode workload), element by element against the whole oracle output."""
     prob = workloads.workload(name)
     say(f"[gpu] full workload {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} {prob.dtype}")
     out = run_gpu(prob, out_fill=float("nan"), splitkv=name in workloads.SPLITKV_WORKLOADS)
     assert bool(torch.isfinite(out).all()), "non-finite values in the output"
-    extra = []
     if prob.mask is not None:
-        dead = torch.nonzero(torch.isinf(prob.mask).all(dim=-1))  # (plane, i)
-        for plane, i in dead.tolist():
-            for h in (0, prob.heads - 1):
-                extra.append((plane, h, i))
         # every (b, h) of a fully masked mask row is exactly zero
+        dead = torch.nonzero(torch.isinf(prob.mask).all(dim=-1))  # (plane, i)
+        assert len(dead) > 0
         for plane, i in dead.tolist():
             if prob.out_layout == "head":
                 assert bool((out[plane, :, i] == 0).all())
-    rows = sample_rows(prob, 384, extra=extra)
-    check(gpu_rows(out, prob, rows), oracle_rows(prob, rows), prob.dtype, name)
+    got = out.double().cpu().numpy()
+    del out
+    check(got, oracle_full(prob), prob.dtype, name)
 
 
 # ------------------------------------------------------------------------------------------
@@ -155,6 +155,78 @@ def test_edge_case(name):
     say(f"[gpu] edge {name}: q{tuple(prob.q.shape)} k{tuple(prob.k.shape)} sk={prob.sk} {prob.dtype}")
     got = run_gpu(prob, out_fill=float("nan")).double().cpu().numpy()
     check(got, oracle_full(prob), prob.dtype, name, amp=EDGE[name].get("amp", 1.0))
+
+
+# ------------------------------------------------------------------------------------------
+# key-rule edges that the workloads never reach (their lengths keep total = past + Sq <= Sk),
+# for every kernel family.  The rule is that of flash_attention_body on the flash_attention.rs
+# page: logical length capped at sk, causal limit past + i (else L - Sq + i), window start
+# causal limit + 1 - W.
+
+KEY_RULE = {
+    # past and total drawn independently, total up to the capacity: rows whose causal limit
+    # passes L - 1, batches whose total is below their past, totals past sk (rows >= sk NaN)
+    "indep_causal": dict(causal=True, lengths="indep", max_past=500, nan_beyond_total=True),
+    # the same with a window: rows whose window starts past L - 1 attend nothing
+    "indep_causal_window": dict(causal=True, local_window=48, lengths="indep", max_past=500,
+                                nan_beyond_total=True),
+    # total above sk (below the capacity) without past lengths: L capped at sk and the causal
+    # base L - Sq; cache rows at and past sk are NaN
+    "total_beyond_sk": dict(causal=True, lengths="explicit", total_values=[640, 512, 301, 0],
+                            nan_beyond_total=True, sk=300),
+    # zero and negative lengths, with a window
+    "zero_and_negative_lengths": dict(causal=True, local_window=100, lengths="explicit",
+                                      total_values=[0, -7, 250, 400],
+                                      past_values=[-5, 3, -300, 390], nan_beyond_total=True),
+}
+
+FAMILIES = {
+    "ring_bf16_d128": dict(dtype="bf16", dim=128),
+    "ring_f16_d64": dict(dtype="f16", dim=64),
+    "fwd16_bf16_d96": dict(dtype="bf16", dim=96),
+    # contiguous but not 16-byte aligned: the ring kernel's alignment gate sends these to fwd16
+    "fwd16_misaligned_f16_d128": dict(dtype="f16", dim=128, misalign=True),
+    "fwd16_misaligned_bf16_d64": dict(dtype="bf16", dim=64, misalign=True),
+    "fp32_d64": dict(dtype="f32", dim=64),
+    "fp32_misaligned_d128": dict(dtype="f32", dim=128, misalign=True),
+    "fp32_wide_d200": dict(dtype="f32", dim=200),
+}
+
+
+@pytest.mark.parametrize("family", list(FAMILIES))
+@pytest.mark.parametrize("rule", list(KEY_RULE))
+def test_key_rule_edges(rule, family):
+    fam = dict(FAMILIES[family])
+    misalign = fam.pop("misalign", False)
+    params = dict(seed=100 + list(KEY_RULE).index(rule), batch=4, heads=8, kv_heads=2, sq=300,
+                  sk=400, kv_capacity=640, **fam)
+    params.update(KEY_RULE[rule])
+    prob = workloads.make_problem(name=f"{rule}-{family}", **params)
+    say(f"[gpu] key rule {rule} / {family}: q{tuple(prob.q.shape)} sk={prob.sk} "
+        f"total={None if prob.total_lengths is None else prob.total_lengths.tolist()} "
+        f"past={None if prob.past_lengths is None else prob.past_lengths.tolist()} misalign={misalign}")
+    want = oracle_full(prob)
+    got = run_gpu(prob, out_fill=float("nan"), misalign=misalign).double().cpu().numpy()
+    check(got, want, prob.dtype, f"{rule}-{family}")
+    assert _edge_reached(prob, rule), f"{rule}: the inputs do not reach the edge"
+
+
+def _edge_reached(prob, rule) -> bool:
+    """Whether the drawn lengths reach the edge the case is named for (a property of the
+    inputs, counted from the stated rule)."""
+    total = prob.total_lengths.tolist()
+    past = None if prob.past_lengths is None else prob.past_lengths.tolist()
+    if rule == "total_beyond_sk":
+        return any(t > prob.sk for t in total)
+    if rule == "zero_and_negative_lengths":
+        return min(total) <= 0 and min(past) < 0
+    over = window_past_end = 0
+    for b in range(prob.batch):
+        L = max(min(total[b], prob.sk), 0)
+        cmax_last = past[b] + prob.sq - 1
+        over += cmax_last > L - 1
+        window_past_end += prob.local_window > 0 and cmax_last + 1 - prob.local_window > L - 1
+    return over > 0 and (prob.local_window == 0 or window_past_end > 0)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

@@ -57,6 +57,22 @@ CASES = {
     # keys fewer than one tile, and total lengths of 0 (fully masked rows)
     "bf16_d128_short": dict(seed=75, batch=4, heads=4, kv_heads=1, sq=1, sk=20, dim=128,
                             dtype="bf16", lengths="total"),
+    # key-rule edges: past and total drawn independently (total up to the capacity, so causal
+    # limits pass L - 1 and totals pass sk; cache rows at and past min(total, sk) are NaN)
+    "bf16_d128_indep_lengths": dict(seed=150, batch=4, heads=8, kv_heads=2, sq=2, sk=700,
+                                    kv_capacity=900, dim=128, dtype="bf16", causal=True,
+                                    lengths="indep", max_past=800, nan_beyond_total=True),
+    # totals above sk without past lengths (L capped at sk, causal base L - sq), with a window
+    "f16_d64_total_beyond_sk_window": dict(seed=151, batch=4, heads=4, kv_heads=2, sq=3, sk=500,
+                                           kv_capacity=768, dim=64, dtype="f16", causal=True,
+                                           local_window=200, lengths="explicit",
+                                           total_values=[768, 600, 501, 17],
+                                           nan_beyond_total=True),
+    # zero and negative lengths; windows that start past the length
+    "bf16_d64_zero_negative_lengths": dict(seed=152, batch=4, heads=8, kv_heads=2, sq=2, sk=1000,
+                                           dim=64, dtype="bf16", causal=True, local_window=64,
+                                           lengths="explicit", total_values=[0, -4, 300, 1000],
+                                           past_values=[-3, 5, 900, 995], nan_beyond_total=True),
 }
 
 

@@ -10,8 +10,11 @@ Recipe (the same for every workload):
     by round-to-nearest-even through ``torch.Tensor.to``.  The device and the oracle consume
     the same rounded values.
   * KV-cache prefill: ``past[b] ~ U{0..max_past}`` (inclusive), ``total = past + Sq``;
-    K/V rows at or beyond ``total[b]`` are filled with NaN, so a kernel that reads and uses
-    them cannot match.
+    K/V rows at or beyond ``min(total[b], Sk)`` are filled with NaN, so a kernel that reads and
+    uses them cannot match.
+  * Key-rule edges: ``past`` and ``total`` drawn independently (``total`` up to the capacity, so
+    it can fall short of ``past + Sq`` or pass ``Sk``), or given explicitly (zero and negative
+    values included).
   * Masked workload: an fp32 additive mask ``[B, Sq, Sk]`` with i.i.d. Bernoulli(p) entries set
     to ``-inf`` (else ``0.0``), plus a few seeded query rows per batch set entirely to ``-inf``.
 """
@@ -131,6 +134,9 @@ def make_problem(
     dist: str = "normal",
     lengths: Optional[str] = None,
     max_past: int = 0,
+    max_total: Optional[int] = None,
+    total_values=None,
+    past_values=None,
     nan_beyond_total: bool = False,
     mask: Optional[str] = None,
     mask_planes: Optional[int] = None,
@@ -142,7 +148,11 @@ def make_problem(
     """Draw one problem.
 
     ``lengths``: ``None`` (no length tensors), ``"past"`` (past ~ U{0..max_past}, total = past + sq),
-    ``"total"`` (only total_lengths ~ U{0..sk}) or ``"past_only"`` (only past_lengths).
+    ``"total"`` (only total_lengths ~ U{0..sk}), ``"past_only"`` (only past_lengths),
+    ``"indep"`` (past ~ U{0..max_past} and, drawn after it, total ~ U{0..max_total}, max_total
+    defaulting to the capacity) or ``"explicit"`` (``total_values`` / ``past_values``, either
+    may be None; no numbers are drawn).
+    ``nan_beyond_total``: K/V rows at or past ``min(total[b], sk)`` become NaN.
     ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0) or ``"normal"``
     (finite N(0,1) values with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
     ``dead_rows``: query rows per mask plane set entirely to -inf.
@@ -163,12 +173,21 @@ def make_problem(
         total = torch.from_numpy(rng.integers(0, sk, size=batch, endpoint=True).astype(np.int32))
     elif lengths == "past_only":
         past = torch.from_numpy(rng.integers(0, max_past, size=batch, endpoint=True).astype(np.int32))
+    elif lengths == "indep":
+        past = torch.from_numpy(rng.integers(0, max_past, size=batch, endpoint=True).astype(np.int32))
+        hi = capacity if max_total is None else max_total
+        total = torch.from_numpy(rng.integers(0, hi, size=batch, endpoint=True).astype(np.int32))
+    elif lengths == "explicit":
+        if total_values is not None:
+            total = torch.tensor(list(total_values), dtype=torch.int32)
+        if past_values is not None:
+            past = torch.tensor(list(past_values), dtype=torch.int32)
     elif lengths is not None:
         raise ValueError(f"unknown lengths recipe {lengths!r}")
 
     if nan_beyond_total and total is not None:
         for b in range(batch):
-            t = int(total[b])
+            t = max(min(int(total[b]), sk), 0)
             if t < capacity:
                 k[b, :, t:, :] = float("nan")
                 v[b, :, t:, :] = float("nan")
