@@ -146,6 +146,21 @@ EDGE = {
                                    softcap=3.0),
     "fp32_d129_token_major": dict(seed=53, batch=2, heads=3, kv_heads=3, sq=65, sk=65, dim=129,
                                   dtype="f32", out_layout="token"),
+    # scores that drift by hundreds along the keys (rising for some rows, falling for others):
+    # later half-tiles exceed the running maximum far beyond the lazy-rescale bound, and their
+    # weights against the old maximum overflow fp32 (head dims 128 and 64, with and without a
+    # causal rule, a softcap that keeps them bounded, and an additive mask that ramps up)
+    "key_ramp_bf16_d128": dict(seed=54, batch=2, heads=4, kv_heads=2, sq=300, sk=520, dim=128,
+                               dtype="bf16", key_ramp=0.5),
+    "key_ramp_f16_d64_causal": dict(seed=55, batch=2, heads=4, kv_heads=1, sq=520, sk=520, dim=64,
+                                    dtype="f16", key_ramp=0.25, causal=True),
+    "key_ramp_bf16_d128_softcap": dict(seed=56, batch=1, heads=4, kv_heads=2, sq=260, sk=400,
+                                       dim=128, dtype="bf16", key_ramp=0.5, softcap=30.0),
+    "mask_ramp_bf16_d64": dict(seed=57, batch=2, heads=2, kv_heads=2, sq=300, sk=512, dim=64,
+                               dtype="bf16", mask="ramp", mask_ramp=0.75, mask_p=0.1),
+    "mask_ramp_f16_d128_f16mask": dict(seed=58, batch=2, heads=2, kv_heads=1, sq=200, sk=448,
+                                        dim=128, dtype="f16", mask="ramp", mask_ramp=0.5,
+                                        mask_p=0.05, mask_planes=1, mask_dtype="f16"),
 }
 
 

@@ -77,7 +77,7 @@ __device__ __forceinline__ void launder(MaskHalf<MASKK>& m) {
 }
 
 // parts of a pipelined block (see the block body)
-constexpr int kBlkPV = 1, kBlkQK = 2, kBlkSM = 4, kBlkEnd = 8;
+constexpr int kBlkPV = 1, kBlkQK = 2, kBlkSM = 4, kBlkEnd = 8, kBlkExact = 16;
 
 // SOFTCAP: 0 none, 1 tanh_fast, 2 tanh_identity (softcap <= kTanhIdentityMaxCap).
 template <typename Tr, int DP, int MASKK, int SOFTCAP, bool RAW, int RB>
@@ -106,9 +106,10 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
     // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
-    // a step's mask values as well and keep fewer, so that no register spills (a spill copy of a
-    // register that an asm load has not filled yet would save stale data)
-    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? (SOFTCAP ? 6 : 8) : 12;
+    // a step's mask values as well, and the head-dim-128 variants with the series tanh or a
+    // scale multiply keep fewer too, so that no register spills (a spill copy of a register that an asm load has
+    // not filled yet would save stale data)
+    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? 6 : ((SOFTCAP == 1 || (SOFTCAP == 0 && !RAW)) && DP == 128 ? 10 : 12);
     constexpr int NPRE = 4 * NDB < AHEAD ? 4 * NDB : AHEAD;   // V reads a block issues for the next one
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
@@ -359,13 +360,17 @@ fwd16_ring_kernel(const FwdParams p) {
     }
 
     f32x16 o[RB][NDB];
-    float m_run[RB], l_run[RB];
+    // running maximum m (-inf: no key yet), denominator, and the exponent offset the weights
+    // are taken against: m_safe = m (0 while m is -inf) and nmk = -m_safe * k
+    float m_run[RB], l_run[RB], m_safe_run[RB], nmk_run[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i) o[rb][i] = f32x16(0.0f);
         m_run[rb] = neg_inf();
         l_run[rb] = 0.0f;
+        m_safe_run[rb] = 0.0f;
+        nmk_run[rb] = 0.0f;
     }
 
     // The item's tile t sits at ring position ring_base + t.  A step issues ring position
@@ -480,18 +485,49 @@ fwd16_ring_kernel(const FwdParams p) {
         }
     };
 
-    // Softmax of half-tile u split in 8 phases so that it can be spread between MFMAs:
-    //   0, 1: epilogue and maximum of elements 0..7 / 8..15; 2: row maximum across the two
-    //   lanes of the row, lazy move of the running maximum; 3..6: exponentials of four elements
-    //   each; 7: 16-bit packing and the denominator.  FULL: the half-tile needs no structural mask.
-    struct SoftmaxState {
-        float mt, alpha, m_safe, nmk, lsum;
-        uint32_t keep;
-        bool moved;
+    // Softmax of half-tile u split in 8 phases so that it can be spread between MFMAs.
+    // FULL: the half-tile needs no structural mask.  Two forms:
+    //   EXACT (an item's first half-tile): 0, 1: epilogue and maximum of elements 0..7 / 8..15;
+    //   2: row maximum across the two lanes of the row, lazy move of the running maximum (only
+    //   when the half-tile raises it by more than 2^kRescaleLog2 in weight); 3..6: exponentials
+    //   of four elements each; 7: 16-bit packing and the denominator.
+    //   Speculative (every later half-tile): no maximum is formed.  The weights are taken
+    //   against the running maximum as it stands, p = 2^(x k - m k), which stays valid as long as
+    //   no weight grows past kSpecBound (relative rounding of the 16-bit weights does not depend
+    //   on their size).  Phases 3..6 keep the exponents a = x k - m k in the score registers and
+    //   pack the weights of each phase one phase later; phase 7 sums the lane's 16 packed
+    //   weights.  A lane sum above kSpecBound (which any weight above it implies), an overflow,
+    //   or a row with no running maximum yet sends the wave through fix_up after the block: it
+    //   takes the row maximum A of the kept exponents, moves the running maximum by A / k and
+    //   recomputes the weights as 2^(a - A), with O and the denominator scaled by 2^-A.
+    // The weights of a half-tile live as 8 words of two 16-bit values (elements 2j, 2j + 1 in word
+    // j % 4 of pf[j / 4]); the P.V products take pf[i] whole as their B operand.  A word is
+    // copied into a scalar before it is reinterpreted: __builtin_bit_cast applied directly to a
+    // vector element reads the vector's first element whatever the index.
+    // weights v, v + 1 (v even), rounded to the input type, into their word
+    auto set_pair = [](u32x4 (&pf)[2], int v, float p0, float p1) __attribute__((always_inline)) {
+        pf[v >> 3][(v & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, vec2));
     };
-    auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, vec8 (&pf)[2],
-                             SoftmaxState& st) __attribute__((always_inline)) {
+    // sum of the 16 packed weights (exact products, fp32 accumulation)
+    auto sum_packed = [](const u32x4 (&pf)[2], float lsum) __attribute__((always_inline)) -> float {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t w = pf[q >> 2][q & 3];
+            lsum = Tr::sum2(__builtin_bit_cast(vec2, w), lsum);
+        }
+        return lsum;
+    };
+    struct SoftmaxState {
+        float mt, alpha, m_safe, nmk, lsum, l_prev;
+        float pt[4];   // speculative: weights of the last four exponentials, not yet packed
+        uint32_t keep;
+        bool moved;   // EXACT: the running maximum moved
+        bool redo;    // speculative: the row needs fix_up
+    };
+    auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, u32x4 (&pf)[2],
+                             SoftmaxState& st, auto exact_c) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
+        constexpr bool EXACT = decltype(exact_c)::value;
         constexpr int rb = decltype(rb_c)::value;
         if (ph == 0 || ph == 1) {
             if (ph == 0) {
@@ -516,8 +552,35 @@ fwd16_ring_kernel(const FwdParams p) {
                     x = __uint_as_float((sel & __float_as_uint(x)) | (~sel & 0xff800000u));
                 }
                 sc[v] = x;
-                st.mt = __builtin_fmaxf(st.mt, x);
+                if constexpr (EXACT) st.mt = __builtin_fmaxf(st.mt, x);
             }
+        } else if (ph == 2 && !EXACT) {
+            st.m_safe = m_safe_run[rb];
+            st.nmk = nmk_run[rb];
+        } else if (ph <= 6 && !EXACT) {
+            // weights of the previous phase's four elements are packed here, a phase (one MFMA)
+            // after their exponentials were issued, so the packing never waits for them
+            if (ph > 3) {
+                const int v0 = 4 * (ph - 4);
+                set_pair(pf, v0, st.pt[0], st.pt[1]);
+                set_pair(pf, v0 + 2, st.pt[2], st.pt[3]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * (ph - 3) + e;
+                float a;
+                if constexpr (SUB_FIRST) a = (sc[v] - st.m_safe) * kfac;
+                else a = __builtin_fmaf(sc[v], kfac, st.nmk);
+                sc[v] = a;   // exponents overwrite the scores (fix_up reads them)
+                st.pt[e] = exp2_hw(a);
+            }
+        } else if (ph == 7 && !EXACT) {
+            set_pair(pf, 12, st.pt[0], st.pt[1]);
+            set_pair(pf, 14, st.pt[2], st.pt[3]);
+            const float lsum = sum_packed(pf, 0.0f);
+            st.l_prev = l_run[rb];
+            l_run[rb] += lsum;
+            st.redo = !(lsum <= kSpecBound) || m_run[rb] == neg_inf();
         } else if (ph == 2) {
             const float mt = half_swap_max(st.mt);
             const bool need = mt > m_run[rb] + th_x;
@@ -527,6 +590,8 @@ fwd16_ring_kernel(const FwdParams p) {
             m_run[rb] = m_new;
             st.m_safe = (m_new == neg_inf()) ? 0.0f : m_new;
             st.nmk = -st.m_safe * kfac;
+            m_safe_run[rb] = st.m_safe;
+            nmk_run[rb] = st.nmk;
             st.lsum = l_run[rb] * st.alpha;
         } else if (ph <= 6) {
 #pragma unroll
@@ -538,13 +603,49 @@ fwd16_ring_kernel(const FwdParams p) {
                 sc[v] = pv_;   // probabilities overwrite the scores
             }
         } else {
-            pf[0] = __builtin_convertvector(__builtin_shufflevector(sc, sc, 0, 1, 2, 3, 4, 5, 6, 7), vec8);
-            pf[1] = __builtin_convertvector(__builtin_shufflevector(sc, sc, 8, 9, 10, 11, 12, 13, 14, 15), vec8);
-            float lsum = st.lsum;
+            pf[0] = __builtin_bit_cast(u32x4, __builtin_convertvector(__builtin_shufflevector(sc, sc, 0, 1, 2, 3, 4, 5, 6, 7), vec8));
+            pf[1] = __builtin_bit_cast(u32x4, __builtin_convertvector(__builtin_shufflevector(sc, sc, 8, 9, 10, 11, 12, 13, 14, 15), vec8));
+            l_run[rb] = sum_packed(pf, st.lsum);
+        }
+    };
+
+    // Speculative softmax of half-tile u in row block rb went wrong for some row of the wave (see
+    // SoftmaxState): recompute the row's weights from the exponents left in sc against their
+    // row maximum A, move the running maximum by A / k and scale O and the denominator by 2^-A
+    // (by 0 for a row without a running maximum so far, whose O and denominator are 0).  A row
+    // whose largest exponent is at most kRescaleLog2 / 2 keeps its weights (a flagged row's
+    // lane sum above kSpecBound over 16 weights needs a weight above kSpecBound / 16, far above
+    // 2^(kRescaleLog2 / 2)), unless it had no running maximum.
+    auto fix_up = [&](auto rb_c, f32x16& sc, u32x4 (&pf)[2], SoftmaxState& st) __attribute__((always_inline)) {
+        constexpr int rb = decltype(rb_c)::value;
+        float am = neg_inf();
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                lsum = Tr::sum2(vec2{pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]}, lsum);
-            l_run[rb] = lsum;
+        for (int v = 0; v < 16; ++v) am = __builtin_fmaxf(am, sc[v]);
+        const float A = half_swap_max(am);
+        const bool empty = m_run[rb] == neg_inf();
+        const bool doit = A > kRescaleLog2 * 0.5f || (empty && A != neg_inf());
+        // (rows that stay without a key, such as fully masked ones, change nothing)
+        if (!wave_any(doit)) return;
+        const float Ause = doit ? A : 0.0f;
+        const float alpha = doit ? (empty ? 0.0f : exp2_hw(-A)) : 1.0f;
+        if (doit) {
+            m_run[rb] = st.m_safe + A / kfac;
+            m_safe_run[rb] = m_run[rb];
+            nmk_run[rb] = st.nmk - A;
+        }
+        u32x4 np[2];
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) set_pair(np, v, exp2_hw(sc[v] - Ause), exp2_hw(sc[v + 1] - Ause));
+        const float lsum = sum_packed(np, 0.0f);
+        if (doit) {
+            pf[0] = np[0];
+            pf[1] = np[1];
+            l_run[rb] = st.l_prev * alpha + lsum;
+        }
+        // (rows without a running maximum have O = 0: only moved ones need the scaling)
+        if (wave_any(doit && !empty)) {
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) o[rb][i] *= alpha;
         }
     };
 
@@ -575,12 +676,14 @@ fwd16_ring_kernel(const FwdParams p) {
     // half-tile -1; in an item's last step the Q.K products (and the second block's softmax)
     // would score half-tiles past the item.  kBlkEnd: no block follows in this item.
     auto xbody = [&](auto full_c, auto mode_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
-                     f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], vec8 (&p_prev)[RB][2], vec8 (&p_cur)[RB][2],
+                     f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], u32x4 (&p_prev)[RB][2], u32x4 (&p_cur)[RB][2],
                      const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE], auto&& unit_hook) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_c)::value;
         constexpr bool WITH_PV = (MODE & kBlkPV) != 0;
         constexpr bool WITH_QK = (MODE & kBlkQK) != 0;
         constexpr bool WITH_SM = (MODE & kBlkSM) != 0;
+        // the exact softmax for an item's first half-tile (no P.V part) and where asked for
+        constexpr bool EXACT_SM = (MODE & kBlkExact) != 0 || !WITH_PV;
         constexpr int PAR = decltype(par_c)::value;
         constexpr int NPV = WITH_PV ? 2 * NDB : 0;   // V^T fragments (one per P.V MFMA per row block)
         constexpr int NQK = WITH_QK ? NKS : 0;       // K fragments
@@ -657,7 +760,7 @@ fwd16_ring_kernel(const FwdParams p) {
             }
             if constexpr (f < NPV) {
                 constexpr int j = f / NDB, db = f % NDB;
-                o[rb][db] = Tr::mfma(__builtin_bit_cast(vec8, frag), p_prev[rb][j], o[rb][db]);
+                o[rb][db] = Tr::mfma(__builtin_bit_cast(vec8, frag), __builtin_bit_cast(vec8, p_prev[rb][j]), o[rb][db]);
             } else {
                 constexpr int ks = f - NPV;
                 s_nxt[rb] = Tr::mfma(__builtin_bit_cast(vec8, frag), qf[rb][ks], ks == 0 ? f32x16(0.0f) : s_nxt[rb]);
@@ -667,7 +770,8 @@ fwd16_ring_kernel(const FwdParams p) {
                 static_for<m * 8 * RB / NM, (m + 1) * 8 * RB / NM>([&](auto q_c) __attribute__((always_inline)) {
                     constexpr int q = decltype(q_c)::value;
                     constexpr int srb = q % RB;
-                    softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb]);
+                    softmax_phase(full_c, int_c<srb>{}, q / RB, u, s_cur[srb], mh[srb], p_cur[srb], st[srb],
+                                  bool_c<EXACT_SM>{});
                 });
             }
             unit_hook(m_c);
@@ -681,17 +785,21 @@ fwd16_ring_kernel(const FwdParams p) {
                 // Keep the probabilities and the row sum inside this block: otherwise they are
                 // sunk past the rescale branch below, next to the next block's P.V products that
                 // consume them, and no longer overlap this block's MFMAs.
-                u32x4 a = __builtin_bit_cast(u32x4, p_cur[rb][0]), c = __builtin_bit_cast(u32x4, p_cur[rb][1]);
-                asm volatile("" : "+v"(a), "+v"(c), "+v"(l_run[rb]));
-                p_cur[rb][0] = __builtin_bit_cast(vec8, a);
-                p_cur[rb][1] = __builtin_bit_cast(vec8, c);
+                asm volatile("" : "+v"(p_cur[rb][0]), "+v"(p_cur[rb][1]), "+v"(l_run[rb]));
             }
+            if constexpr (EXACT_SM) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                if (wave_any(st[rb].moved)) {
+                for (int rb = 0; rb < RB; ++rb) {
+                    if (wave_any(st[rb].moved)) {
 #pragma unroll
-                    for (int i = 0; i < NDB; ++i) o[rb][i] *= st[rb].alpha;
+                        for (int i = 0; i < NDB; ++i) o[rb][i] *= st[rb].alpha;
+                    }
                 }
+            } else {
+                static_for<0, RB>([&](auto rb_c) __attribute__((always_inline)) {
+                    constexpr int rb = decltype(rb_c)::value;
+                    if (wave_any(st[rb].redo)) fix_up(rb_c, s_cur[rb], p_cur[rb], st[rb]);
+                });
             }
         }
     };
@@ -705,28 +813,32 @@ fwd16_ring_kernel(const FwdParams p) {
     // for them (and tile t+2) right after it.
     //
     // Kinds of step: 0 skip (no half-tile of the step's blocks is attended by the wave: no
-    // compute, P = 0), 1 masked, 2 full (both blocks need no structural mask).  Steps go in
+    // compute, P = 0), 1 masked, 2 full (both blocks need no structural mask), 3 masked with the
+    // exact softmax: the leading masked steps of a wave, where rows that have attended nothing
+    // yet take their first keys (with the speculative softmax every such row would need the
+    // fix-up; the exact form sets their maximum directly).  Steps go in
     // pairs (2p, 2p+1) so that the mask buffers alternate statically; along p a wave's pairs
     // run skip, masked, full, masked, skip, each kind in a loop of its own (no branch on the
     // kind inside a loop, so the compiler keeps one register assignment per loop).
     constexpr bool MASK_AHEAD = MASKED && DP == 64;
     f32x16 s_even[RB], s_odd[RB];
-    vec8 p_even[RB][2], p_odd[RB][2];
+    u32x4 p_even[RB][2], p_odd[RB][2];
     u32x2 rpre[NPRE];   // leading V operand reads of the next block, issued by the block before
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) rpre[i] = u32x2{0u, 0u};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         s_even[rb] = s_odd[rb] = f32x16(0.0f);
-        p_even[rb][0] = p_even[rb][1] = p_odd[rb][0] = p_odd[rb][1] = vec8((scalar)0.0f);
+        p_even[rb][0] = p_even[rb][1] = p_odd[rb][0] = p_odd[rb][1] = u32x4{0u, 0u, 0u, 0u};
     }
     MaskH mask_a[2][RB], mask_b[2][RB];   // [half parity][row block]: odd half-tile first
     // PHASE 0: step -1 (Q.K of half-tiles 0 and 1, softmax of half-tile 0); 1: any other step.
     auto step = [&](auto kind_c, auto phase_c, int t, MaskH (&mcur)[2][RB], MaskH (&mnext)[2][RB]) __attribute__((always_inline)) {
         constexpr int KIND = decltype(kind_c)::value;
         constexpr int PHASE = decltype(phase_c)::value;
-        constexpr int MODE_A = PHASE == 0 ? kBlkQK : kBlkPV | kBlkQK | kBlkSM;
-        constexpr int MODE_B = PHASE == 0 ? kBlkQK | kBlkSM : kBlkPV | kBlkQK | kBlkSM;
+        constexpr int EX = KIND == 3 ? kBlkExact : 0;
+        constexpr int MODE_A = PHASE == 0 ? kBlkQK : kBlkPV | kBlkQK | kBlkSM | EX;
+        constexpr int MODE_B = PHASE == 0 ? kBlkQK | kBlkSM : kBlkPV | kBlkQK | kBlkSM | EX;
         // unmasked step -1: tiles 0 .. 2 are issued and tiles 0 and 1 landed and visible before
         // it, so it issues no loads and runs into step 0 without a wait or a barrier
         constexpr bool EARLY = PHASE == 0 && !MASKED;
@@ -745,7 +857,7 @@ fwd16_ring_kernel(const FwdParams p) {
             dma_issue_all(dp);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = vec8((scalar)0.0f);
+                p_odd[rb][0] = p_odd[rb][1] = p_even[rb][0] = p_even[rb][1] = u32x4{0u, 0u, 0u, 0u};
             // the next step's first block expects its leading V reads in flight
             const uint32_t vn_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
             static_for<0, NPRE>([&](auto r_c) __attribute__((always_inline)) {
@@ -850,13 +962,13 @@ fwd16_ring_kernel(const FwdParams p) {
         step(int_c<1>{}, int_c<0>{}, -1, mask_b, mask_a);
         if constexpr (!MASKED) {
             run_steps(int_c<0>{}, 0, a0);
-            run_steps(int_c<1>{}, a0, f0);
+            run_steps(int_c<3>{}, a0, f0);
             run_steps(int_c<2>{}, f0, f1);
             run_steps(int_c<1>{}, f1, a1);
             run_steps(int_c<0>{}, a1, n_steps);
         } else {
             run_pairs(int_c<0>{}, 0, a0);
-            run_pairs(int_c<1>{}, a0, f0);
+            run_pairs(int_c<3>{}, a0, f0);
             run_pairs(int_c<2>{}, f0, f1);
             run_pairs(int_c<1>{}, f1, a1);
             run_pairs(int_c<0>{}, a1, n_pairs);

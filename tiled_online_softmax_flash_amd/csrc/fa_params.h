@@ -16,6 +16,10 @@ constexpr int kWideThreads = 384;
 // Lazy rescaling threshold, in log2 units: the running row maximum is only moved when a
 // new score exceeds it by more than this, so unnormalised probabilities stay <= 2^8.
 constexpr float kRescaleLog2 = 8.0f;
+// The speculative softmax of the ring kernel lets weights grow to 2^14 against a stale running
+// maximum before it moves the maximum (a lane's sum of 16 weights above kSpecBound); 2^14 keeps
+// every weight finite in f16 (largest finite value 65504) and in fp32 sums.
+constexpr float kSpecBound = 16384.0f;
 
 struct FwdParams {
     const void* q;               // [batch, heads, sq, dim]

@@ -138,10 +138,12 @@ def make_problem(
     total_values=None,
     past_values=None,
     nan_beyond_total: bool = False,
+    key_ramp: float = 0.0,
     mask: Optional[str] = None,
     mask_planes: Optional[int] = None,
     mask_dtype: str = "f32",
     mask_p: float = 0.1,
+    mask_ramp: float = 0.0,
     dead_rows: int = 0,
     out_layout: str = "head",
 ) -> Problem:
@@ -153,8 +155,12 @@ def make_problem(
     defaulting to the capacity) or ``"explicit"`` (``total_values`` / ``past_values``, either
     may be None; no numbers are drawn).
     ``nan_beyond_total``: K/V rows at or past ``min(total[b], sk)`` become NaN.
-    ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0) or ``"normal"``
-    (finite N(0,1) values with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
+    ``key_ramp``: ``key_ramp * j`` is added to every element of key row j before rounding, so
+    that scores drift by a large amount along the keys (rising for some query rows, falling for
+    others).
+    ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0), ``"normal"``
+    (finite N(0,1) values with Bernoulli -inf holes) or ``"ramp"`` (``mask_ramp * j`` for key j,
+    with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
     ``dead_rows``: query rows per mask plane set entirely to -inf.
     ``dist``: ``"normal"`` (N(0,1)) or ``"neg_uniform"`` (U[-1,0)), times ``amp``.
     """
@@ -163,6 +169,9 @@ def make_problem(
     q = _normal(rng, (batch, heads, sq, dim), dtype, amp, dist)
     k = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
     v = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
+    if key_ramp:
+        ramp = torch.arange(capacity, dtype=torch.float32).view(1, 1, capacity, 1) * np.float32(key_ramp)
+        k = (k.float() + ramp).to(k.dtype)
 
     total = past = None
     if lengths == "past":
@@ -200,6 +209,9 @@ def make_problem(
             m = np.zeros((planes, sq, sk), dtype=np.float32)
         elif mask == "normal":
             m = rng.standard_normal(size=(planes, sq, sk), dtype=np.float32)
+        elif mask == "ramp":
+            m = np.broadcast_to(np.arange(sk, dtype=np.float32) * np.float32(mask_ramp),
+                                (planes, sq, sk)).copy()
         else:
             raise ValueError(f"unknown mask recipe {mask!r}")
         m[holes] = -np.inf
