@@ -158,6 +158,18 @@ EDGE = {
                                        dim=128, dtype="bf16", key_ramp=0.5, softcap=30.0),
     "mask_ramp_bf16_d64": dict(seed=57, batch=2, heads=2, kv_heads=2, sq=300, sk=512, dim=64,
                                dtype="bf16", mask="ramp", mask_ramp=0.75, mask_p=0.1),
+    # masks at the end of the float32 range: rows whose attended keys all hold the most
+    # negative finite value get a uniform softmax (not zeros), and that value loses to 0 or to
+    # half of it; the running maximum sits near -3.4e38, where its exponent offset overflows
+    "mask_extreme_bf16_d64": dict(seed=59, batch=2, heads=2, kv_heads=1, sq=90, sk=300, dim=64,
+                                  dtype="bf16", mask="extreme", mask_p=0.05, causal=True),
+    "mask_extreme_f16_d128": dict(seed=60, batch=1, heads=3, kv_heads=3, sq=70, sk=200, dim=128,
+                                  dtype="f16", mask="extreme", mask_p=0.05),
+    "mask_extreme_bf16_d96_bf16mask": dict(seed=61, batch=2, heads=2, kv_heads=2, sq=60, sk=160,
+                                           dim=96, dtype="bf16", mask="extreme", mask_p=0.05,
+                                           mask_dtype="bf16"),
+    "mask_extreme_fp32": dict(seed=62, batch=1, heads=2, kv_heads=1, sq=50, sk=130, dim=64,
+                              dtype="f32", mask="extreme", mask_p=0.05),
     "mask_ramp_f16_d128_f16mask": dict(seed=58, batch=2, heads=2, kv_heads=1, sq=200, sk=448,
                                         dim=128, dtype="f16", mask="ramp", mask_ramp=0.5,
                                         mask_p=0.05, mask_planes=1, mask_dtype="f16"),

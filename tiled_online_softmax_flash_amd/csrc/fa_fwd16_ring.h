@@ -492,14 +492,13 @@ fwd16_ring_kernel(const FwdParams p) {
     //   when the half-tile raises it by more than 2^kRescaleLog2 in weight); 3..6: exponentials
     //   of four elements each; 7: 16-bit packing and the denominator.
     //   Speculative (every later half-tile): no maximum is formed.  The weights are taken
-    //   against the running maximum as it stands, p = 2^(x k - m k), which stays valid as long as
-    //   no weight grows past kSpecBound (relative rounding of the 16-bit weights does not depend
-    //   on their size).  Phases 3..6 keep the exponents a = x k - m k in the score registers and
-    //   pack the weights of each phase one phase later; phase 7 sums the lane's 16 packed
-    //   weights.  A lane sum above kSpecBound (which any weight above it implies), an overflow,
-    //   or a row with no running maximum yet sends the wave through fix_up after the block: it
-    //   takes the row maximum A of the kept exponents, moves the running maximum by A / k and
-    //   recomputes the weights as 2^(a - A), with O and the denominator scaled by 2^-A.
+    //   against the running maximum as it stands, p = 2^(x k - m k), which stays valid as long
+    //   as no weight grows past kSpecBound
+    //   (relative rounding of the 16-bit weights does not depend on their size).  Phases 3..6
+    //   leave the scores in sc and pack the weights of each phase one phase later; phase 7 sums
+    //   the lane's 16 packed weights.  A lane sum above kSpecBound (which any weight above it
+    //   implies), a non-finite sum, or a row with no running maximum yet sends the wave through
+    //   fix_up after the block, which redoes the half-tile exactly for the rows concerned.
     // The weights of a half-tile live as 8 words of two 16-bit values (elements 2j, 2j + 1 in word
     // j % 4 of pf[j / 4]); the P.V products take pf[i] whole as their B operand.  A word is
     // copied into a scalar before it is reinterpreted: __builtin_bit_cast applied directly to a
@@ -568,11 +567,12 @@ fwd16_ring_kernel(const FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * (ph - 3) + e;
-                float a;
-                if constexpr (SUB_FIRST) a = (sc[v] - st.m_safe) * kfac;
-                else a = __builtin_fmaf(sc[v], kfac, st.nmk);
-                sc[v] = a;   // exponents overwrite the scores (fix_up reads them)
-                st.pt[e] = exp2_hw(a);
+                // (the scores stay in sc for fix_up).  With an additive mask the running maximum
+                // can be huge (masks near the float range's end), where -m k carries a rounding
+                // error far above 1: the difference is formed before scaling, as in the exact
+                // form.  Without one, scores and thus m k stay moderate and one multiply-add does.
+                if constexpr (SUB_FIRST) st.pt[e] = exp2_hw((sc[v] - st.m_safe) * kfac);
+                else st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
             }
         } else if (ph == 7 && !EXACT) {
             set_pair(pf, 12, st.pt[0], st.pt[1]);
@@ -610,32 +610,34 @@ fwd16_ring_kernel(const FwdParams p) {
     };
 
     // Speculative softmax of half-tile u in row block rb went wrong for some row of the wave (see
-    // SoftmaxState): recompute the row's weights from the exponents left in sc against their
-    // row maximum A, move the running maximum by A / k and scale O and the denominator by 2^-A
-    // (by 0 for a row without a running maximum so far, whose O and denominator are 0).  A row
-    // whose largest exponent is at most kRescaleLog2 / 2 keeps its weights (a flagged row's
-    // lane sum above kSpecBound over 16 weights needs a weight above kSpecBound / 16, far above
-    // 2^(kRescaleLog2 / 2)), unless it had no running maximum.
+    // SoftmaxState): for each flagged row (either of its lanes flagged) that has or gets a key,
+    // take the row maximum of the half-tile's scores (still in sc), move the running maximum to
+    // it if it is larger, and recompute the row's weights as 2^((x - m) k) with the difference
+    // formed before scaling (safe for scores near the float range's end, as in the exact form);
+    // O and the denominator are scaled by 2^((m_old - m) k), or by 0 for a row that had no key.
     auto fix_up = [&](auto rb_c, f32x16& sc, u32x4 (&pf)[2], SoftmaxState& st) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_c)::value;
         float am = neg_inf();
 #pragma unroll
         for (int v = 0; v < 16; ++v) am = __builtin_fmaxf(am, sc[v]);
-        const float A = half_swap_max(am);
+        const float ax = half_swap_max(am);
+        const uint32_t flag = st.redo ? 1u : 0u;
+        const auto fl = __builtin_amdgcn_permlane32_swap(flag, flag, false, false);
         const bool empty = m_run[rb] == neg_inf();
-        const bool doit = A > kRescaleLog2 * 0.5f || (empty && A != neg_inf());
         // (rows that stay without a key, such as fully masked ones, change nothing)
+        const bool doit = (fl[0] | fl[1]) != 0u && (ax != neg_inf() || !empty);
         if (!wave_any(doit)) return;
-        const float Ause = doit ? A : 0.0f;
-        const float alpha = doit ? (empty ? 0.0f : exp2_hw(-A)) : 1.0f;
+        const float m_new = doit ? (empty ? ax : __builtin_fmaxf(m_run[rb], ax)) : 0.0f;
+        const float alpha = doit ? (empty ? 0.0f : exp2_hw((m_run[rb] - m_new) * kfac)) : 1.0f;
         if (doit) {
-            m_run[rb] = st.m_safe + A / kfac;
-            m_safe_run[rb] = m_run[rb];
-            nmk_run[rb] = st.nmk - A;
+            m_run[rb] = m_new;
+            m_safe_run[rb] = m_new;
+            nmk_run[rb] = -m_new * kfac;
         }
         u32x4 np[2];
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) set_pair(np, v, exp2_hw(sc[v] - Ause), exp2_hw(sc[v + 1] - Ause));
+        for (int v = 0; v < 16; v += 2)
+            set_pair(np, v, exp2_hw((sc[v] - m_new) * kfac), exp2_hw((sc[v + 1] - m_new) * kfac));
         const float lsum = sum_packed(np, 0.0f);
         if (doit) {
             pf[0] = np[0];

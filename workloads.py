@@ -159,8 +159,9 @@ def make_problem(
     that scores drift by a large amount along the keys (rising for some query rows, falling for
     others).
     ``mask``: ``None``, ``"bernoulli"`` (-inf with probability ``mask_p``, else 0), ``"normal"``
-    (finite N(0,1) values with Bernoulli -inf holes) or ``"ramp"`` (``mask_ramp * j`` for key j,
-    with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
+    (finite N(0,1) values with Bernoulli -inf holes), ``"ramp"`` (``mask_ramp * j`` for key j,
+    with Bernoulli -inf holes) or ``"extreme"`` (finite values at the end of the mask type's
+    range, see below, with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
     ``dead_rows``: query rows per mask plane set entirely to -inf.
     ``dist``: ``"normal"`` (N(0,1)) or ``"neg_uniform"`` (U[-1,0)), times ``amp``.
     """
@@ -212,6 +213,15 @@ def make_problem(
         elif mask == "ramp":
             m = np.broadcast_to(np.arange(sk, dtype=np.float32) * np.float32(mask_ramp),
                                 (planes, sq, sk)).copy()
+        elif mask == "extreme":
+            # finite values at the end of the mask type's range: row i % 3 == 0 holds only the
+            # most negative finite value, row 1 mixes it with 0, row 2 mixes it with half of it
+            big = np.float32(torch.finfo(_TORCH_DTYPES[mask_dtype]).max)
+            pick = rng.random(size=(planes, sq, sk), dtype=np.float32) < np.float32(0.5)
+            m = np.full((planes, sq, sk), -big, dtype=np.float32)
+            m[:, 1::3, :] = np.where(pick[:, 1::3, :], np.float32(0.0), -big)
+            m[:, 2::3, :] = np.where(pick[:, 2::3, :], -big / np.float32(2.0), -big)
+            del pick
         else:
             raise ValueError(f"unknown mask recipe {mask!r}")
         m[holes] = -np.inf
