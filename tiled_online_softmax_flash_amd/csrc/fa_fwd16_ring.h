@@ -522,6 +522,7 @@ fwd16_ring_kernel(const FwdParams p) {
         uint32_t keep;
         bool moved;   // EXACT: the running maximum moved
         bool redo;    // speculative: the row needs fix_up
+        bool big;     // speculative, masked: the row's exponent offset is too large to fold in
     };
     auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, u32x4 (&pf)[2],
                              SoftmaxState& st, auto exact_c) __attribute__((always_inline)) {
@@ -556,6 +557,13 @@ fwd16_ring_kernel(const FwdParams p) {
         } else if (ph == 2 && !EXACT) {
             st.m_safe = m_safe_run[rb];
             st.nmk = nmk_run[rb];
+            // One multiply-add forms x k - m k with nmk = -m k rounded once: an error of at most
+            // |m k| 2^-24 in every exponent of the row, a common factor that cancels.  With an
+            // additive mask the running maximum can be huge (masks near the float range's end)
+            // and that error far above 1: such rows (|m k| > kSpecOffsetMax) always go through
+            // fix_up, which forms the difference before scaling.  Without a mask the scores, and
+            // so m k, stay moderate.
+            if constexpr (MASKED) st.big = !(__builtin_fabsf(st.nmk) <= kSpecOffsetMax);
         } else if (ph <= 6 && !EXACT) {
             // weights of the previous phase's four elements are packed here, a phase (one MFMA)
             // after their exponentials were issued, so the packing never waits for them
@@ -567,12 +575,8 @@ fwd16_ring_kernel(const FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * (ph - 3) + e;
-                // (the scores stay in sc for fix_up).  With an additive mask the running maximum
-                // can be huge (masks near the float range's end), where -m k carries a rounding
-                // error far above 1: the difference is formed before scaling, as in the exact
-                // form.  Without one, scores and thus m k stay moderate and one multiply-add does.
-                if constexpr (SUB_FIRST) st.pt[e] = exp2_hw((sc[v] - st.m_safe) * kfac);
-                else st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
+                // (the scores stay in sc for fix_up)
+                st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
             }
         } else if (ph == 7 && !EXACT) {
             set_pair(pf, 12, st.pt[0], st.pt[1]);
@@ -581,6 +585,7 @@ fwd16_ring_kernel(const FwdParams p) {
             st.l_prev = l_run[rb];
             l_run[rb] += lsum;
             st.redo = !(lsum <= kSpecBound) || m_run[rb] == neg_inf();
+            if constexpr (MASKED) st.redo = st.redo || st.big;
         } else if (ph == 2) {
             const float mt = half_swap_max(st.mt);
             const bool need = mt > m_run[rb] + th_x;

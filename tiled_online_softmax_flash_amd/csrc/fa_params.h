@@ -20,6 +20,9 @@ constexpr float kRescaleLog2 = 8.0f;
 // maximum before it moves the maximum (a lane's sum of 16 weights above kSpecBound); 2^14 keeps
 // every weight finite in f16 (largest finite value 65504) and in fp32 sums.
 constexpr float kSpecBound = 16384.0f;
+// Largest exponent offset |m k| the speculative softmax folds into one multiply-add (its rounding
+// error, at most 2^12 * 2^-24, is negligible); rows beyond it take the exact fix-up.
+constexpr float kSpecOffsetMax = 4096.0f;
 
 struct FwdParams {
     const void* q;               // [batch, heads, sq, dim]
