@@ -36,6 +36,13 @@ from tiled_online_softmax_flash_amd.metrics import attended_counts, problem_work
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# Exponentials per second: the fp32 vector peak of 157.3 TFLOP/s counts a packed fused
+# multiply-add (2 lanes x 2 flops) per lane slot, i.e. 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# = 39.3 T plain lane operations per second; transcendental instructions (v_exp_f32) issue at
+# half that rate on gfx950 (a microbenchmark of independent v_exp_f32 chains measures 3.2 plain
+# multiply-adds' worth of time each, at the box's own clock).  The softmax takes one exponential
+# per attended score, the secondary ceiling the attention kernels are held to.
+PEAK_EXP_PER_S = 256 * 4 * 16 * 2.4e9 / 2
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk_eff·D) + % of MI355X MFMA peak"
 KERNEL_SOURCES = ["fa_device.h", "fa_params.h", "fa_fwd16.h", "fa_fwd16_ring.h",
                   "fa_fwd16_ring_consts.h", "fa_fwd32.h", "fa_fwd32w.h", "fa_splitkv.h",
@@ -364,6 +371,13 @@ def main(argv=None) -> int:
             "algorithmic_flops_per_launch": work["flops"],
             "algorithmic_bytes_per_launch": work["bytes"],
             "hbm_gbs_at_algorithmic_bytes": round(work["bytes"] / (kern_avg_ms * 1e-3) / 1e9, 1),
+            # secondary ceiling: one exponential per attended score against the exp issue rate
+            "exp_ceiling": {
+                "achieved": round(work["attended_scores"] / (kern_avg_ms * 1e-3) / 1e12, 3),
+                "peak": round(PEAK_EXP_PER_S / 1e12, 2),
+                "unit": "T exp/s",
+                "frac": round(work["attended_scores"] / (kern_avg_ms * 1e-3) / PEAK_EXP_PER_S, 4),
+            },
         },
         "cpu_baseline": None,
     }
