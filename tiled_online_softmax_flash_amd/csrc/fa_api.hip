@@ -115,7 +115,9 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
                  aligned(out, 16) && (sk == 0 || (aligned(k, 16) && aligned(v, 16))) &&
                  (mask_planes == 0 || mask_vec) && (int64_t)kv_capacity * dim * 2 < 0x7fffffffLL;
     plan->wide = dtype == FA_DTYPE_F32 && dim > 128;
-    const int block_rows = plan->ring ? fa::kRingBlockRows : (plan->wide ? fa::kWideRows : fa::kBlockRows);
+    const int block_rows = plan->ring ? fa::kRingBlockRows
+                           : plan->wide ? fa::kWideRows
+                           : dtype == FA_DTYPE_F32 ? fa::kF32Rows : fa::kBlockRows;
     if (mask_planes > 0 && (int64_t)block_rows * sk * 4 >= 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "sk %d is too long for a masked launch (a workgroup's mask rows "
                     "must span less than 2 GiB)", sk);

@@ -1,32 +1,56 @@
-// Tiled online-softmax attention forward for fp32 inputs on gfx950.
+// Tiled online-softmax attention forward for fp32 inputs with head dims up to 128 on gfx950.
 //
-// Same structure as the 16-bit kernel (fa_fwd16.h), with every value kept in fp32 as the
-// pictor-kernels page `src/gpu_backend/cuda_imagen_attn_kernels.rs` requires of its
-// parity-first path (no reduced-precision staging of Q, K, V, S or P).  The contractions run
-// on v_mfma_f32_32x32x2_f32 (full fp32 products, fp32 accumulation); K/V tiles of 32 keys
-// are staged in LDS (K row-permuted, V transposed), double-buffered.
+// Every value stays in fp32, as the pictor-kernels page `src/gpu_backend/cuda_imagen_attn_kernels.rs`
+// requires of its parity-first path (no reduced-precision staging of Q, K, V, S or P).  The
+// contractions run on v_mfma_f32_16x16x4_f32 (full fp32 products, fp32 accumulation), so a wave
+// owns 16 query rows and a workgroup of four waves 64 rows.  fp32 problems are small in rows per
+// flop: at 32 rows per wave a 24-head, 1536-row problem makes 1152 waves for 1024 SIMDs, and
+// most SIMDs run a single wave that cannot hide its own latency; 16-row waves double the count.
+//
+// Lane l = 16 s + r of a wave stands for query row r of the wave and k-slot s (0..3):
+//   * S^T = K Q^T, one MFMA per 4 dims: lane (r, s) supplies K[key r][dim s DP/4 + c] and
+//     Q[row r][dim s DP/4 + c] at step c, and ends with the scores of keys 4s..4s+3 of row r.
+//   * O^T += V^T P^T, one MFMA per 4 keys and 16 dims: lane (r, s) supplies V[key 4s+v][dim]
+//     and its own weight P[row r][key 4s+v] at step v, and accumulates O[row r][16 db + 4s + i].
+// A row's statistics are reduced over its four lanes r, r+16, r+32, r+48 with permlane swaps.
+// Tiles of 16 keys are staged in LDS through registers (K row-major, V transposed so that a
+// lane's four keys of one dim are one 16-byte read), double-buffered with one barrier per tile.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_device.h"
 
 namespace fa {
 
+// max / sum over the four lanes r, r + 16, r + 32, r + 48 (every lane gets the result).
+__device__ __forceinline__ float row4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_max(__builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return half_swap_sum(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+}
+
 // RAW: no mask, no softcap and scale > 0 (scale folded into the base-2 exponent factor).
 template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3)))
 fwd32_kernel(const FwdParams p) {
-    constexpr int BN = 32;
+    constexpr int BN = 16;              // keys per tile
+    constexpr int WR = 16;              // query rows per wave
     constexpr int KP = DP + 4;          // K tile row pitch (floats): 16-byte pad
     constexpr int VP = BN + 4;          // V^T tile row pitch (floats): 16-byte pad
     constexpr int KSZ = BN * KP;
     constexpr int VSZ = DP * VP;
-    constexpr int NQC = DP / 8;         // 8-dim chunks of the QK reduction
-    constexpr int NDB = DP / 32;
-    constexpr int CPR = DP / 4;         // 16-byte chunks per K row
-    constexpr int NKC = BN * CPR / 256;
-    constexpr int NVBLK = (BN / 4) * (DP / 4);
-    constexpr int NVB = (NVBLK + 255) / 256;
+    constexpr int QS = DP / 4;          // dims of one k-slot
+    constexpr int NQ = DP / 16;         // 16-byte pieces of a k-slot
+    constexpr int NDB = DP / 16;        // 16-dim output blocks
+    constexpr int CPR = DP / 4;         // 16-byte chunks per K/V row
+    constexpr int NCH = BN * CPR;       // chunks per K (or V) tile
+    constexpr int NLD = (NCH + kThreads - 1) / kThreads;
     static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
+    static_assert(kF32Rows == 4 * WR && kThreads == 256, "four 16-row waves");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * (KSZ + VSZ)];
 
@@ -37,17 +61,18 @@ fwd32_kernel(const FwdParams p) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
     const int lane = tid & 63;
-    const int lr = lane & 31;
-    const int hh = lane >> 5;
+    const int r = lane & 15;
+    const int s = lane >> 4;
     const int D = p.dim;
 
     const KeyRule rule = make_rule(p, b);
-    const int64_t q0 = (int64_t)w.qt * kBlockRows;
-    const int64_t q_last = (q0 + kBlockRows < p.sq ? q0 + kBlockRows : p.sq) - 1;
-    const int64_t wr0 = q0 + wave * kWaveRows;
+    const int Lk = (int)rule.L;         // keys < sk <= INT32_MAX
+    const int64_t q0 = (int64_t)w.qt * kF32Rows;
+    const int64_t q_last = (q0 + kF32Rows < p.sq ? q0 + kF32Rows : p.sq) - 1;
+    const int64_t wr0 = q0 + wave * WR;
     const bool wave_has_rows = wr0 < p.sq;
-    const int64_t wr1 = (wr0 + kWaveRows - 1 < p.sq ? wr0 + kWaveRows - 1 : p.sq - 1);
-    const int64_t row = wr0 + lr;
+    const int64_t wr1 = (wr0 + WR - 1 < p.sq ? wr0 + WR - 1 : p.sq - 1);
+    const int64_t row = wr0 + r;
     const bool row_valid = row < p.sq;
     const int64_t my_lo = row_valid ? rule.lo(row) : 1;
     const int64_t my_hi = row_valid ? rule.hi(row) : 0;
@@ -65,13 +90,13 @@ fwd32_kernel(const FwdParams p) {
     const float* __restrict__ kg = (const float*)p.k + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * D;
     const float* __restrict__ vg = (const float*)p.v + ((int64_t)b * p.kv_heads + kvh) * p.kv_capacity * D;
 
-    // ---- Q: lane (m, hh) holds Q[row][8*c + 4*hh + e], e = 0..3 (k-slot hh of step 4c+e)
-    f32x4 qf[NQC];
+    // ---- Q: lane (r, s) holds Q[row][s*QS + 4c + e] in qf[c][e]
+    f32x4 qf[NQ];
     {
         const float* qrow = (const float*)p.q + (((int64_t)b * p.heads + h) * p.sq + (row_valid ? row : 0)) * D;
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-            const int d0 = 8 * c + 4 * hh;
+        for (int c = 0; c < NQ; ++c) {
+            const int d0 = s * QS + 4 * c;
             f32x4 val = f32x4(0.0f);
             if (row_valid && p.vec_kv && d0 < D) {
                 val = *(const f32x4*)(qrow + d0);
@@ -88,59 +113,50 @@ fwd32_kernel(const FwdParams p) {
     if (MASKED)
         mrow = (const float*)p.mask + (mask_plane(p, b, h) * p.sq + (row_valid ? row : 0)) * (int64_t)p.sk;
 
-    f32x16 o[NDB];
+    f32x4 o[NDB];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) o[i] = f32x16(0.0f);
+    for (int i = 0; i < NDB; ++i) o[i] = f32x4(0.0f);
     float m_run = neg_inf();
-    float l_run = 0.0f;
+    float l_run = 0.0f;  // this lane's share (keys 4s..4s+3 of every tile) of the row's sum
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
-    f32x4 kreg[NKC];
-    f32x4 vreg[NVB][4];
-
-    auto load_tile = [&](int kt) {
+    // Does tile kt hold a key that some row of this wave attends?
+    auto wave_needs = [&](int kt) -> bool {
         const int64_t k0 = (int64_t)kt * BN;
+        return wave_has_rows && k0 <= w_hi_max && k0 + BN - 1 >= w_lo_min && w_lo_min <= w_hi_max;
+    };
+
+    // Tile loads: chunk u (16 bytes) of K is row u / CPR, dims 4 (u % CPR)..; chunk u of V is
+    // key u % BN, dims 4 (u / BN).. (key-fastest, so that the transposed LDS writes of a
+    // half-wave fall in 32 different banks).  Keys at or past L and dims at or past D load 0.
+    // VEC: rows move in 16-byte pieces (D a multiple of 4, aligned pointers).
+    f32x4 kreg[NLD], vreg[NLD];
+    auto load_chunk = [&](auto vec_tag, const float* src, bool ok, int col) -> f32x4 {
+        f32x4 val = f32x4(0.0f);
+        if (ok) {
+            if constexpr (decltype(vec_tag)::value) {
+                val = *(const f32x4*)src;
+            } else {
 #pragma unroll
-        for (int n = 0; n < NKC; ++n) {
-            const int c = tid + 256 * n;
-            const int krow = c / CPR;
-            const int kcol = (c % CPR) * 4;
-            const int64_t j = k0 + krow;
-            f32x4 val = f32x4(0.0f);
-            if (j < rule.L && kcol < D) {
-                const float* src = kg + j * D + kcol;
-                if (p.vec_kv) {
-                    val = *(const f32x4*)src;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (kcol + e < D) val[e] = src[e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < D) val[e] = src[e];
             }
-            kreg[n] = val;
         }
+        return val;
+    };
+    auto load_tile = [&](auto vec_tag, int kt) {
+        const int k0 = kt * BN;
+        const float* kt_g = kg + (int64_t)k0 * D;
+        const float* vt_g = vg + (int64_t)k0 * D;
 #pragma unroll
-        for (int n = 0; n < NVB; ++n) {
-            const int blk = tid + 256 * n;
-            const int kq = blk & 7;
-            const int dq = blk >> 3;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t j = k0 + 4 * kq + e;
-                f32x4 val = f32x4(0.0f);
-                if ((NVBLK % 256 == 0 || blk < NVBLK) && j < rule.L && 4 * dq < D) {
-                    const float* src = vg + j * D + 4 * dq;
-                    if (p.vec_kv) {
-                        val = *(const f32x4*)src;
-                    } else {
-#pragma unroll
-                        for (int x = 0; x < 4; ++x)
-                            if (4 * dq + x < D) val[x] = src[x];
-                    }
-                }
-                vreg[n][e] = val;
-            }
+        for (int n = 0; n < NLD; ++n) {
+            const int u = tid + kThreads * n;
+            const bool in = NCH % kThreads == 0 || u < NCH;
+            const int kr = u / CPR, kc = (u % CPR) * 4;
+            kreg[n] = load_chunk(vec_tag, kt_g + kr * D + kc, in && k0 + kr < Lk && kc < D, kc);
+            const int vr = u % BN, vc = (u / BN) * 4;
+            vreg[n] = load_chunk(vec_tag, vt_g + vr * D + vc, in && k0 + vr < Lk && vc < D, vc);
         }
     };
 
@@ -148,63 +164,47 @@ fwd32_kernel(const FwdParams p) {
         float* kl = lds + buf * (KSZ + VSZ);
         float* vl = kl + KSZ;
 #pragma unroll
-        for (int n = 0; n < NKC; ++n) {
-            const int c = tid + 256 * n;
-            const int krow = c / CPR;
-            const int kcol = (c % CPR) * 4;
-            *(f32x4*)(kl + lds_row_of_key(krow) * KP + kcol) = kreg[n];
-        }
+        for (int n = 0; n < NLD; ++n) {
+            const int u = tid + kThreads * n;
+            if (NCH % kThreads != 0 && u >= NCH) continue;
+            *(f32x4*)(kl + (u / CPR) * KP + (u % CPR) * 4) = kreg[n];
+            const int vr = u % BN, vc = (u / BN) * 4;
 #pragma unroll
-        for (int n = 0; n < NVB; ++n) {
-            const int blk = tid + 256 * n;
-            if (NVBLK % 256 == 0 || blk < NVBLK) {
-                const int kq = blk & 7;
-                const int dq = blk >> 3;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *(f32x4*)(vl + (4 * dq + c) * VP + 4 * kq) =
-                        f32x4{vreg[n][0][c], vreg[n][1][c], vreg[n][2][c], vreg[n][3][c]};
-            }
+            for (int e = 0; e < 4; ++e) vl[(vc + e) * VP + vr] = vreg[n][e];
         }
     };
 
-    auto compute_tile = [&](int buf, int kt) {
+    // mask[row][keys 4s..4s+3 of tile kt]
+    auto load_mask = [&](int kt) -> f32x4 {
+        f32x4 val = f32x4(0.0f);
+        if (row_valid) {
+            const int j = kt * BN + 4 * s;
+            if (p.vec_mask && j + 3 < p.sk) {
+                val = *(const f32x4*)(mrow + j);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < p.sk) val[e] = mrow[j + e];
+            }
+        }
+        return val;
+    };
+
+    auto compute_tile = [&](int buf, int kt, const f32x4& mval) {
         const int64_t k0 = (int64_t)kt * BN;
         const int64_t k1 = k0 + BN - 1;
-        if (!wave_has_rows || k0 > w_hi_max || k1 < w_lo_min || w_lo_min > w_hi_max) return;
         const bool full = k0 >= w_lo_max && k1 <= w_hi_min;
         const float* kl = lds + buf * (KSZ + VSZ);
         const float* vl = kl + KSZ;
 
-        float mval[16];
-        if (MASKED) {
-            const int64_t jb = k0 + 16 * hh;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t j = jb + 4 * c;
-                f32x4 val = f32x4(0.0f);
-                if (row_valid) {
-                    if (p.vec_mask && j + 3 < p.sk) {
-                        val = *(const f32x4*)(mrow + j);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (j + e < p.sk) val[e] = mrow[j + e];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mval[4 * c + e] = val[e];
-            }
-        }
-
         // S^T = K Q^T
-        f32x16 s = f32x16(0.0f);
+        f32x4 sc = f32x4(0.0f);
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-            const f32x4 a = *(const f32x4*)(kl + lr * KP + 8 * c + 4 * hh);
+        for (int c = 0; c < NQ; ++c) {
+            const f32x4 a = *(const f32x4*)(kl + r * KP + s * QS + 4 * c);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf[c][e], sc, 0, 0, 0);
         }
 
         auto epi = [&](float sv, float mv) -> float {
@@ -220,24 +220,24 @@ fwd32_kernel(const FwdParams p) {
         float mt = neg_inf();
         if (full) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float x = epi(s[v], MASKED ? mval[v] : 0.0f);
-                s[v] = x;
+            for (int i = 0; i < 4; ++i) {
+                const float x = epi(sc[i], MASKED ? mval[i] : 0.0f);
+                sc[i] = x;
                 mt = __builtin_fmaxf(mt, x);
             }
         } else {
-            const int base = (int)k0 + 16 * hh;
+            const int base = (int)k0 + 4 * s;
             const int lo_rel = my_lo32 - base;
             const int hi_rel = my_hi32 - base;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = epi(s[v], MASKED ? mval[v] : 0.0f);
-                x = (v >= lo_rel && v <= hi_rel) ? x : neg_inf();
-                s[v] = x;
+            for (int i = 0; i < 4; ++i) {
+                float x = epi(sc[i], MASKED ? mval[i] : 0.0f);
+                x = (i >= lo_rel && i <= hi_rel) ? x : neg_inf();
+                sc[i] = x;
                 mt = __builtin_fmaxf(mt, x);
             }
         }
-        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+        mt = row4_max(mt);
 
         const bool need = mt > m_run + th_x;
         if (wave_any(need)) {
@@ -251,69 +251,74 @@ fwd32_kernel(const FwdParams p) {
 
         const float mk = m_run * kfac;
         const bool slow = (mk == neg_inf() || mk == -neg_inf()) && m_run != neg_inf();
-        float pv[16];
+        float pv[4];
         if (!wave_any(slow)) {
             const float nmk = (m_run == neg_inf()) ? 0.0f : -mk;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                pv[v] = exp2_hw(__builtin_fmaf(s[v], kfac, nmk));
-                l_run += pv[v];
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = exp2_hw(__builtin_fmaf(sc[i], kfac, nmk));
+                l_run += pv[i];
             }
         } else {
             const float mr = (m_run == neg_inf()) ? 0.0f : m_run;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                pv[v] = exp2_hw((s[v] - mr) * kfac);
-                l_run += pv[v];
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = exp2_hw((sc[i] - mr) * kfac);
+                l_run += pv[i];
             }
         }
 
-        // O^T += V^T P^T : step t uses key 16*hh + t in k-slot hh
+        // O^T += V^T P^T
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
+            const f32x4 a = *(const f32x4*)(vl + (16 * db + r) * VP + 4 * s);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 a = *(const f32x4*)(vl + (32 * db + lr) * VP + 16 * hh + 4 * q4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], pv[4 * q4 + e], o[db], 0, 0, 0);
-            }
+            for (int v = 0; v < 4; ++v)
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], pv[v], o[db], 0, 0, 0);
         }
     };
 
-    if (n_tiles > 0) {
-        load_tile(kt_begin);
+    auto main_loop = [&](auto vec_tag) {
+        f32x4 mcur = f32x4(0.0f);
+        if (MASKED && wave_needs(kt_begin)) mcur = load_mask(kt_begin);
+        load_tile(vec_tag, kt_begin);
         store_tile(0);
         __syncthreads();
         for (int t = 0; t < n_tiles; ++t) {
             const int cur = t & 1;
-            if (t + 1 < n_tiles) load_tile(kt_begin + t + 1);
-            compute_tile(cur, kt_begin + t);
+            const int kt = kt_begin + t;
+            f32x4 mnext = f32x4(0.0f);
+            if (t + 1 < n_tiles) {
+                load_tile(vec_tag, kt + 1);
+                if (MASKED && wave_needs(kt + 1)) mnext = load_mask(kt + 1);
+            }
+            if (wave_needs(kt)) compute_tile(cur, kt, mcur);
             if (t + 1 < n_tiles) store_tile(cur ^ 1);
             __syncthreads();
+            mcur = mnext;
         }
+    };
+    if (n_tiles > 0) {
+        if (p.vec_kv) main_loop(std::true_type{});
+        else main_loop(std::false_type{});
     }
 
+    // every lane takes part in the row sums before the invalid rows leave
+    const float l = row4_sum(l_run);
     if (!row_valid) return;
-    const float l = l_run + __shfl_xor(l_run, 32);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float* orow = (float*)p.out + (int64_t)b * p.o_stride_b + (int64_t)h * p.o_stride_h + row * p.o_stride_i;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+        const int d = 16 * db + 4 * s;
+        if (d >= D) continue;
+        const f32x4 val = o[db] * inv;
+        if (p.vec_out) {
+            *(f32x4*)(orow + d) = val;
+        } else {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int d = 32 * db + 8 * a + 4 * hh;
-            if (d >= D) continue;
-            f32x4 val;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) val[c] = o[db][4 * a + c] * inv;
-            if (p.vec_out) {
-                *(f32x4*)(orow + d) = val;
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (d + c < D) orow[d + c] = val[c];
-            }
+            for (int c = 0; c < 4; ++c)
+                if (d + c < D) orow[d + c] = val[c];
         }
     }
 }

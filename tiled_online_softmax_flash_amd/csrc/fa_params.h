@@ -5,10 +5,12 @@
 
 namespace fa {
 
-// Rows per workgroup for every kernel: four 64-lane waves of 32 query rows each.
+// Rows per workgroup of the 16-bit kernel of fa_fwd16.h: four 64-lane waves of 32 query rows each.
 constexpr int kBlockRows = 128;
 constexpr int kWaveRows = 32;
 constexpr int kThreads = 256;
+// fp32 kernel for head dims up to 128 (fa_fwd32.h): 64 rows per workgroup, four waves of 16 rows
+constexpr int kF32Rows = 64;
 // fp32 kernel for head dims 129..384 (fa_fwd32w.h): 64 rows per workgroup, six waves
 constexpr int kWideRows = 64;
 constexpr int kWideThreads = 384;
@@ -34,7 +36,7 @@ struct FwdParams {
     void* out;
     int batch, heads, kv_heads, sq, sk, dim, group;
     int causal, window, mask_planes;
-    int q_tiles;                 // ceil(sq / kBlockRows)
+    int q_tiles;                 // ceil(sq / rows per workgroup of the kernel)
     int pairs;                   // batch * q_tiles: (batch, query tile) pairs
     int xcd_groups;              // 1: group-major workgroup order (see decode_work)
     int items_per_xcd;           // work items per XCD (the non-persistent grid / 8)
