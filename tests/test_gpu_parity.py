@@ -170,6 +170,25 @@ EDGE = {
                                            mask_dtype="bf16"),
     "mask_extreme_fp32": dict(seed=62, batch=1, heads=2, kv_heads=1, sq=50, sk=130, dim=64,
                               dtype="f32", mask="extreme", mask_p=0.05),
+    # fp32: scores that keep rising along the keys make the running maximum stale tile after
+    # tile (the kernel's exact redo; the ramp keeps the scores' own fp32 rounding, about 2e-5 in
+    # the output, inside the gate).  Zero queries with masks offset by thousands make the scores
+    # the exact mask values at |m log2 e| above 4096, where the weights are formed by
+    # subtracting before scaling.
+    "key_ramp_fp32_d128": dict(seed=63, batch=2, heads=4, kv_heads=2, sq=300, sk=520, dim=128,
+                               dtype="f32", key_ramp=0.05),
+    "key_ramp_fp32_d64_causal_softcap": dict(seed=64, batch=1, heads=4, kv_heads=2, sq=330,
+                                             sk=330, dim=64, dtype="f32", key_ramp=0.25,
+                                             causal=True, softcap=30.0),
+    "mask_offset_fp32_d128_ramp": dict(seed=65, batch=1, heads=3, kv_heads=3, sq=130, sk=512,
+                                       dim=128, dtype="f32", mask="ramp", mask_ramp=0.002,
+                                       mask_offset=3000.0, mask_p=0.1, q_scale=0.0),
+    "mask_offset_fp32_d72_causal": dict(seed=66, batch=2, heads=2, kv_heads=1, sq=200, sk=300,
+                                        dim=72, dtype="f32", mask="normal", mask_offset=-6000.0,
+                                        mask_p=0.05, causal=True, q_scale=0.0),
+    "mask_ramp_fp32_d72": dict(seed=67, batch=2, heads=2, kv_heads=1, sq=200, sk=300, dim=72,
+                               dtype="f32", mask="ramp", mask_ramp=0.75, mask_p=0.05,
+                               causal=True),
     "mask_ramp_f16_d128_f16mask": dict(seed=58, batch=2, heads=2, kv_heads=1, sq=200, sk=448,
                                         dim=128, dtype="f16", mask="ramp", mask_ramp=0.5,
                                         mask_p=0.05, mask_planes=1, mask_dtype="f16"),

@@ -15,6 +15,14 @@
 // A row's statistics are reduced over its four lanes r, r+16, r+32, r+48 with permlane swaps.
 // Tiles of 16 keys are staged in LDS through registers (K row-major, V transposed so that a
 // lane's four keys of one dim are one 16-byte read), double-buffered with one barrier per tile.
+//
+// On gfx950 an fp32 MFMA and the vector instructions of other waves on the same SIMD do not
+// overlap (measured: every vector instruction adds its own issue time to the MFMA time), so the
+// loop keeps vector work per tile small: tile loads go through buffer descriptors (no address or
+// bounds arithmetic per tile), tile classification is scalar, the loop is unrolled twice so that
+// LDS addresses are constants, and the softmax takes the weights against the running maximum
+// as it stands, without a per-tile row maximum, redoing a tile exactly only when its weights
+// grow too large (see compute_tile).
 #pragma once
 
 #include <type_traits>
@@ -32,6 +40,9 @@ __device__ __forceinline__ float row4_sum(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return half_swap_sum(__uint_as_float(a[0]) + __uint_as_float(a[1]));
 }
+
+// A buffer offset beyond every descriptor's range: loads through it return 0.
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 
 // RAW: no mask, no softcap and scale > 0 (scale folded into the base-2 exponent factor).
 template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
@@ -109,103 +120,133 @@ fwd32_kernel(const FwdParams p) {
         }
     }
 
-    const float* mrow = nullptr;
-    if (MASKED)
-        mrow = (const float*)p.mask + (mask_plane(p, b, h) * p.sq + (row_valid ? row : 0)) * (int64_t)p.sk;
+    // ---- mask rows of this workgroup: one descriptor per tile (its base moves with the tile),
+    // per-lane byte offsets; rows past sq and keys past the rows' end read as 0.  Keys past sk
+    // of a row read the next row's values, which only ever meet keys the key rule excludes.
+    const char* mbase = nullptr;
+    int64_t mask_bytes = 0;
+    uint32_t mask_off = kOutOfRange;
+    if constexpr (MASKED) {
+        mbase = (const char*)p.mask + ((mask_plane(p, b, h) * p.sq + q0) * (int64_t)p.sk) * 4;
+        mask_bytes = (q_last - q0 + 1) * (int64_t)p.sk * 4;   // < 2 GiB (checked by the host)
+        if (row_valid) mask_off = (uint32_t)((row - q0) * (int64_t)p.sk * 4) + 16u * (uint32_t)s;
+    }
 
     f32x4 o[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) o[i] = f32x4(0.0f);
+    // Running state of the row.  nmk = -m_run * kfac while the multiply-add form of the weights
+    // may be used (m_run finite and |m_run kfac| <= kSpecOffsetMax); NaN otherwise, which sends
+    // every tile of the row through the exact softmax.
     float m_run = neg_inf();
+    float nmk = __builtin_nanf("");
     float l_run = 0.0f;  // this lane's share (keys 4s..4s+3 of every tile) of the row's sum
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
-    // Does tile kt hold a key that some row of this wave attends?
-    auto wave_needs = [&](int kt) -> bool {
-        const int64_t k0 = (int64_t)kt * BN;
-        return wave_has_rows && k0 <= w_hi_max && k0 + BN - 1 >= w_lo_min && w_lo_min <= w_hi_max;
-    };
+    // ---- tile ranges of this wave (wave-uniform, 32-bit): tiles holding a key some row of the
+    // wave attends, and tiles whose every key every row of the wave attends
+    int wt_first = 0, wt_last = -1, wf_first = 0, wf_last = -1;
+    if (wave_has_rows && w_lo_min <= w_hi_max) {
+        wt_first = (int)(w_lo_min / BN);
+        wt_last = (int)(w_hi_max / BN);
+        wf_first = (int)((w_lo_max + BN - 1) / BN);
+        wf_last = w_hi_min >= BN - 1 ? (int)((w_hi_min + 1) / BN) - 1 : -1;
+    }
 
-    // Tile loads: chunk u (16 bytes) of K is row u / CPR, dims 4 (u % CPR)..; chunk u of V is
-    // key u % BN, dims 4 (u / BN).. (key-fastest, so that the transposed LDS writes of a
-    // half-wave fall in 32 different banks).  Keys at or past L and dims at or past D load 0.
-    // VEC: rows move in 16-byte pieces (D a multiple of 4, aligned pointers).
-    f32x4 kreg[NLD], vreg[NLD];
-    auto load_chunk = [&](auto vec_tag, const float* src, bool ok, int col) -> f32x4 {
-        f32x4 val = f32x4(0.0f);
-        if (ok) {
-            if constexpr (decltype(vec_tag)::value) {
-                val = *(const f32x4*)src;
-            } else {
+    // ---- per-thread tile layout, fixed for the whole loop.  Chunk u (16 bytes) of K is key
+    // u / CPR, dims 4 (u % CPR)..; chunk u of V is key u % BN, dims 4 (u / BN).. (key-fastest,
+    // so that the transposed LDS writes of a half-wave fall in 32 different banks).  Each tile is
+    // read through a descriptor that ends at key L (or the tile end): keys past L read as 0, and
+    // chunks past the head dim take an offset beyond any descriptor.
+    uint32_t k_off[NLD], v_off[NLD];
+    int k_cnt[NLD], v_cnt[NLD];   // valid floats of the chunk (0..4)
+    int k_lds[NLD], v_lds[NLD];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (col + e < D) val[e] = src[e];
-            }
-        }
-        return val;
-    };
-    auto load_tile = [&](auto vec_tag, int kt) {
+    for (int n = 0; n < NLD; ++n) {
+        const int u = tid + kThreads * n;
+        const bool in = NCH % kThreads == 0 || u < NCH;
+        const int kr = u / CPR, kc = (u % CPR) * 4;
+        const int vr = u % BN, vc = (u / BN) * 4;
+        k_cnt[n] = in ? (D - kc < 0 ? 0 : (D - kc > 4 ? 4 : D - kc)) : 0;
+        v_cnt[n] = in ? (D - vc < 0 ? 0 : (D - vc > 4 ? 4 : D - vc)) : 0;
+        k_off[n] = k_cnt[n] > 0 ? (uint32_t)(kr * D + kc) * 4u : kOutOfRange;
+        v_off[n] = v_cnt[n] > 0 ? (uint32_t)(vr * D + vc) * 4u : kOutOfRange;
+        k_lds[n] = in ? kr * KP + kc : 0;
+        v_lds[n] = in ? vc * VP + vr : 0;
+    }
+
+    f32x4 kreg[NLD], vreg[NLD];
+    auto tile_rsrc = [&](const float* base, int kt) {
         const int k0 = kt * BN;
-        const float* kt_g = kg + (int64_t)k0 * D;
-        const float* vt_g = vg + (int64_t)k0 * D;
+        const int keys = Lk - k0 < BN ? Lk - k0 : BN;   // >= 1 for every loaded tile
+        return make_rsrc(base + (int64_t)k0 * D, keys * D * 4);
+    };
+    // VEC: rows move in 16-byte pieces (D a multiple of 4, aligned pointers); else one float at
+    // a time, floats past the head dim reading as 0.
+    auto load_tile = [&](auto vec_tag, int kt) {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, kt);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vg, kt);
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const int u = tid + kThreads * n;
-            const bool in = NCH % kThreads == 0 || u < NCH;
-            const int kr = u / CPR, kc = (u % CPR) * 4;
-            kreg[n] = load_chunk(vec_tag, kt_g + kr * D + kc, in && k0 + kr < Lk && kc < D, kc);
-            const int vr = u % BN, vc = (u / BN) * 4;
-            vreg[n] = load_chunk(vec_tag, vt_g + vr * D + vc, in && k0 + vr < Lk && vc < D, vc);
+            if constexpr (decltype(vec_tag)::value) {
+                kreg[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[n], 0, 0));
+                vreg[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[n], 0, 0));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kreg[n][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        rk, e < k_cnt[n] ? k_off[n] + 4u * e : kOutOfRange, 0, 0));
+                    vreg[n][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        rv, e < v_cnt[n] ? v_off[n] + 4u * e : kOutOfRange, 0, 0));
+                }
+            }
         }
     };
 
-    auto store_tile = [&](int buf) {
-        float* kl = lds + buf * (KSZ + VSZ);
+    auto store_tile = [&](auto buf_tag) {
+        float* kl = lds + decltype(buf_tag)::value * (KSZ + VSZ);
         float* vl = kl + KSZ;
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const int u = tid + kThreads * n;
-            if (NCH % kThreads != 0 && u >= NCH) continue;
-            *(f32x4*)(kl + (u / CPR) * KP + (u % CPR) * 4) = kreg[n];
-            const int vr = u % BN, vc = (u / BN) * 4;
+            if (NCH % kThreads != 0 && tid + kThreads * n >= NCH) continue;
+            *(f32x4*)(kl + k_lds[n]) = kreg[n];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vl[(vc + e) * VP + vr] = vreg[n][e];
+            for (int e = 0; e < 4; ++e) vl[v_lds[n] + e * VP] = vreg[n][e];
         }
     };
 
     // mask[row][keys 4s..4s+3 of tile kt]
     auto load_mask = [&](int kt) -> f32x4 {
-        f32x4 val = f32x4(0.0f);
-        if (row_valid) {
-            const int j = kt * BN + 4 * s;
-            if (p.vec_mask && j + 3 < p.sk) {
-                val = *(const f32x4*)(mrow + j);
-            } else {
+        const int64_t k0b = (int64_t)kt * BN * 4;
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(mbase + k0b, (int)(mask_bytes - k0b));
+        if (p.vec_mask)
+            return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, mask_off, 0, 0));
+        f32x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j + e < p.sk) val[e] = mrow[j + e];
-            }
-        }
+        for (int e = 0; e < 4; ++e)
+            val[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rm, mask_off == kOutOfRange ? kOutOfRange : mask_off + 4u * e, 0, 0));
         return val;
     };
 
-    auto compute_tile = [&](int buf, int kt, const f32x4& mval) {
-        const int64_t k0 = (int64_t)kt * BN;
-        const int64_t k1 = k0 + BN - 1;
-        const bool full = k0 >= w_lo_max && k1 <= w_hi_min;
-        const float* kl = lds + buf * (KSZ + VSZ);
+    auto compute_tile = [&](auto buf_tag, int kt, const f32x4& mval) {
+        const float* kl = lds + decltype(buf_tag)::value * (KSZ + VSZ);
         const float* vl = kl + KSZ;
 
-        // S^T = K Q^T
-        f32x4 sc = f32x4(0.0f);
+        // S^T = K Q^T, in two interleaved chains (even and odd steps) so that consecutive
+        // MFMAs do not wait on each other's results
+        f32x4 sc = f32x4(0.0f), sc_odd = f32x4(0.0f);
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             const f32x4 a = *(const f32x4*)(kl + r * KP + s * QS + 4 * c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; e += 2) {
                 sc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf[c][e], sc, 0, 0, 0);
+                sc_odd = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e + 1], qf[c][e + 1], sc_odd, 0, 0, 0);
+            }
         }
+        sc += sc_odd;
 
         auto epi = [&](float sv, float mv) -> float {
             if constexpr (SOFTCAP) {
@@ -217,56 +258,58 @@ fwd32_kernel(const FwdParams p) {
                 return RAW ? sv : sv * p.scale;
             }
         };
-        float mt = neg_inf();
-        if (full) {
+        if (kt >= wf_first && kt <= wf_last) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = epi(sc[i], MASKED ? mval[i] : 0.0f);
-                sc[i] = x;
-                mt = __builtin_fmaxf(mt, x);
-            }
+            for (int i = 0; i < 4; ++i) sc[i] = epi(sc[i], MASKED ? mval[i] : 0.0f);
         } else {
-            const int base = (int)k0 + 4 * s;
+            const int base = kt * BN + 4 * s;
             const int lo_rel = my_lo32 - base;
             const int hi_rel = my_hi32 - base;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = epi(sc[i], MASKED ? mval[i] : 0.0f);
-                x = (i >= lo_rel && i <= hi_rel) ? x : neg_inf();
-                sc[i] = x;
-                mt = __builtin_fmaxf(mt, x);
+                const float x = epi(sc[i], MASKED ? mval[i] : 0.0f);
+                sc[i] = (i >= lo_rel && i <= hi_rel) ? x : neg_inf();
             }
         }
-        mt = row4_max(mt);
 
-        const bool need = mt > m_run + th_x;
-        if (wave_any(need)) {
-            const float m_new = need ? mt : m_run;
-            const float alpha = need ? exp2_hw((m_run - m_new) * kfac) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
-        }
-
-        const float mk = m_run * kfac;
-        const bool slow = (mk == neg_inf() || mk == -neg_inf()) && m_run != neg_inf();
+        // Weights against the running maximum as it stands.  The tile is redone exactly when
+        // a lane's four weights sum past kSpecBound (or are not finite, or the row has no usable
+        // maximum yet, nmk = NaN): the row maximum of the tile is taken, the running maximum
+        // moved if the tile's exceeds it by more than kRescaleLog2 (base 2), the row's output
+        // and sum rescaled, and the weights recomputed.
         float pv[4];
-        if (!wave_any(slow)) {
-            const float nmk = (m_run == neg_inf()) ? 0.0f : -mk;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = exp2_hw(__builtin_fmaf(sc[i], kfac, nmk));
-                l_run += pv[i];
-            }
-        } else {
-            const float mr = (m_run == neg_inf()) ? 0.0f : m_run;
+        for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(__builtin_fmaf(sc[i], kfac, nmk));
+        float psum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        if (wave_any(!(psum <= kSpecBound))) {
+            float mt = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
+            mt = row4_max(mt);
+            const bool need = mt > m_run + th_x;
+            if (wave_any(need)) {
+                const float m_new = need ? mt : m_run;
+                const float alpha = need ? exp2_hw((m_run - m_new) * kfac) : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = exp2_hw((sc[i] - mr) * kfac);
-                l_run += pv[i];
+                for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+                l_run *= alpha;
+                m_run = m_new;
             }
+            const float mk = m_run * kfac;
+            const bool fma_form = m_run == neg_inf() || __builtin_fabsf(mk) <= kSpecOffsetMax;
+            nmk = (m_run != neg_inf() && fma_form) ? -mk : __builtin_nanf("");
+            if (!wave_any(!fma_form)) {
+                const float nm = (m_run == neg_inf()) ? 0.0f : -mk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(__builtin_fmaf(sc[i], kfac, nm));
+            } else {
+                // large offsets: subtract before scaling, so that the rounding of m k does not
+                // weigh this row's keys differently from its earlier ones
+                const float mr = (m_run == neg_inf()) ? 0.0f : m_run;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = exp2_hw((sc[i] - mr) * kfac);
+            }
+            psum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         }
+        l_run += psum;
 
         // O^T += V^T P^T
 #pragma unroll
@@ -278,24 +321,31 @@ fwd32_kernel(const FwdParams p) {
         }
     };
 
+    auto wave_needs = [&](int kt) { return kt >= wt_first && kt <= wt_last; };
     auto main_loop = [&](auto vec_tag) {
         f32x4 mcur = f32x4(0.0f);
         if (MASKED && wave_needs(kt_begin)) mcur = load_mask(kt_begin);
         load_tile(vec_tag, kt_begin);
-        store_tile(0);
+        store_tile(std::integral_constant<int, 0>{});
         __syncthreads();
-        for (int t = 0; t < n_tiles; ++t) {
-            const int cur = t & 1;
+        // tile t sits in buffer t % 2; two tiles per trip so that the buffer is a constant
+        auto step = [&](auto buf_tag, int t) {
+            constexpr int BUF = decltype(buf_tag)::value;
             const int kt = kt_begin + t;
+            const bool more = t + 1 < n_tiles;
             f32x4 mnext = f32x4(0.0f);
-            if (t + 1 < n_tiles) {
+            if (more) {
                 load_tile(vec_tag, kt + 1);
                 if (MASKED && wave_needs(kt + 1)) mnext = load_mask(kt + 1);
             }
-            if (wave_needs(kt)) compute_tile(cur, kt, mcur);
-            if (t + 1 < n_tiles) store_tile(cur ^ 1);
+            if (wave_needs(kt)) compute_tile(buf_tag, kt, mcur);
+            if (more) store_tile(std::integral_constant<int, BUF ^ 1>{});
             __syncthreads();
             mcur = mnext;
+        };
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
         }
     };
     if (n_tiles > 0) {
@@ -338,11 +388,12 @@ hipError_t launch_fwd32_dp(const FwdParams& p, int grid, bool masked, bool softc
                         : launch_fwd32_one<DP, false, false, false>(p, grid, s);
 }
 
+// Head dims 65..96 take the 128-dim build (dims past D are zero): a 96-dim build needs more
+// registers than three waves per SIMD allow.
 inline hipError_t launch_fwd32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s) {
     switch (dp) {
         case 32: return launch_fwd32_dp<32>(p, grid, masked, softcap, s);
         case 64: return launch_fwd32_dp<64>(p, grid, masked, softcap, s);
-        case 96: return launch_fwd32_dp<96>(p, grid, masked, softcap, s);
         default: return launch_fwd32_dp<128>(p, grid, masked, softcap, s);
     }
 }

@@ -144,6 +144,8 @@ def make_problem(
     mask_dtype: str = "f32",
     mask_p: float = 0.1,
     mask_ramp: float = 0.0,
+    mask_offset: float = 0.0,
+    q_scale: float = 1.0,
     dead_rows: int = 0,
     out_layout: str = "head",
 ) -> Problem:
@@ -162,6 +164,9 @@ def make_problem(
     (finite N(0,1) values with Bernoulli -inf holes), ``"ramp"`` (``mask_ramp * j`` for key j,
     with Bernoulli -inf holes) or ``"extreme"`` (finite values at the end of the mask type's
     range, see below, with Bernoulli -inf holes); ``mask_planes`` defaults to ``batch``.
+    ``mask_offset``: added (in float32) to the finite values of a ``"normal"`` or ``"ramp"`` mask.
+    ``q_scale``: every element of Q is multiplied by it after the draw (0 gives all-zero scores,
+    so that the scores are the mask values exactly, whatever their magnitude).
     ``dead_rows``: query rows per mask plane set entirely to -inf.
     ``dist``: ``"normal"`` (N(0,1)) or ``"neg_uniform"`` (U[-1,0)), times ``amp``.
     """
@@ -170,6 +175,8 @@ def make_problem(
     q = _normal(rng, (batch, heads, sq, dim), dtype, amp, dist)
     k = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
     v = _normal(rng, (batch, kv_heads, capacity, dim), dtype, amp, dist)
+    if q_scale != 1.0:
+        q = (q.float() * np.float32(q_scale)).to(q.dtype)
     if key_ramp:
         ramp = torch.arange(capacity, dtype=torch.float32).view(1, 1, capacity, 1) * np.float32(key_ramp)
         k = (k.float() + ramp).to(k.dtype)
@@ -224,6 +231,8 @@ def make_problem(
             del pick
         else:
             raise ValueError(f"unknown mask recipe {mask!r}")
+        if mask_offset and mask in ("normal", "ramp"):
+            m = m + np.float32(mask_offset)
         m[holes] = -np.inf
         del holes
         if dead_rows:
