@@ -47,6 +47,25 @@ __device__ __forceinline__ float tanh_identity(float y) {
     return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
+// tanh in terms of z = 2 log2(e) y (the argument of the identity's exponential).
+//   tanh_identity_z: 1 - 2 / (2^z + 1), one exponential and one reciprocal (see tanh_identity).
+//   tanh_series_z, for |y| < 1/8 (|z| < kTanhSeriesMaxZ): the odd series y - y^3/3 + 2 y^5/15
+//   written in z, no transcendental instruction.  Its truncation error is below
+//   (17/315) y^7 <= 2.1e-7 |y| there, under the identity's absolute error of a few ulps of 1.
+constexpr float kTanhZ = 2.0f * kLog2e;
+constexpr float kTanhSeriesMaxZ = kTanhZ / 8.0f;
+__device__ __forceinline__ float tanh_identity_z(float z) {
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_hw(z) + 1.0f);
+}
+__device__ __forceinline__ float tanh_series_z(float z) {
+    constexpr double k = 2.0 * 1.4426950408889634;
+    constexpr float a1 = (float)(1.0 / k);
+    constexpr float a3 = (float)(-1.0 / (3.0 * k * k * k));
+    constexpr float a5 = (float)(2.0 / (15.0 * k * k * k * k * k));
+    const float z2 = z * z;
+    return z * __builtin_fmaf(z2, __builtin_fmaf(z2, a5, a3), a1);
+}
+
 // One workgroup's share of the problem: batch b, query head h, query tile qt.
 struct WorkItem {
     int b, h, qt;

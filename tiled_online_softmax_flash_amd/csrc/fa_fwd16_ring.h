@@ -106,10 +106,10 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
     // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
-    // a step's mask values as well, and the head-dim-128 variants with the series tanh or a
-    // scale multiply keep fewer too, so that no register spills (a spill copy of a register that an asm load has
+    // a step's mask values as well, and the head-dim-128 variants with a softcap or a scale
+    // multiply keep fewer too, so that no register spills (a spill copy of a register that an asm load has
     // not filled yet would save stale data)
-    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? 6 : ((SOFTCAP == 1 || (SOFTCAP == 0 && !RAW)) && DP == 128 ? 10 : 12);
+    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? 6 : ((SOFTCAP != 0 || !RAW) && DP == 128 ? 10 : 12);
     constexpr int NPRE = 4 * NDB < AHEAD ? 4 * NDB : AHEAD;   // V reads a block issues for the next one
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
@@ -138,6 +138,7 @@ fwd16_ring_kernel(const FwdParams p) {
     const int D = DP;
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
+    const float cap_z = p.cap_y * kTanhZ;   // dot product -> argument of tanh_*_z
     const scalar* __restrict__ qg = (const scalar*)p.q;
 
     // ---- DMA source offsets: DMA op i of a tile writes physical 16-byte chunks [64 i, 64 i + 64)
@@ -474,7 +475,7 @@ fwd16_ring_kernel(const FwdParams p) {
     // score epilogue of one element: tracked units x (see RAW / SOFTCAP / MASKED)
     auto epi = [&](float sv, float mvv) __attribute__((always_inline)) -> float {
         if constexpr (SOFTCAP) {
-            const float th = SOFTCAP == 2 ? tanh_identity(sv * p.cap_y) : tanh_fast(sv * p.cap_y);
+            const float th = tanh_fast(sv * p.cap_y);
             return MASKED ? __builtin_fmaf(p.softcap, th, mvv) : th;
         } else if constexpr (MASKED) {
             return __builtin_fmaf(sv, p.scale, mvv);
@@ -542,10 +543,31 @@ fwd16_ring_kernel(const FwdParams p) {
                     st.keep = below_hi & ~below_lo;
                 }
             }
+            // identity-form softcap: the eight tanh arguments of the phase take the series when
+            // all of the wave's are below 1/8 (no transcendental), else the identity
+            float th[8];
+            if constexpr (SOFTCAP == 2) {
+                float z[8];
+                float zmax = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    z[e] = sc[8 * ph + e] * cap_z;
+                    zmax = __builtin_fmaxf(zmax, __builtin_fabsf(z[e]));
+                }
+                if (!wave_any(!(zmax < kTanhSeriesMaxZ))) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) th[e] = tanh_series_z(z[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) th[e] = tanh_identity_z(z[e]);
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int v = 8 * ph + e;
-                float x = epi(sc[v], mask_val(mh, v));
+                float x;
+                if constexpr (SOFTCAP == 2) x = MASKED ? __builtin_fmaf(p.softcap, th[e], mask_val(mh, v)) : th[e];
+                else x = epi(sc[v], mask_val(mh, v));
                 if constexpr (!FULL) {
                     // all ones where element v is kept, else zero; masked elements become -inf
                     const uint32_t sel = (uint32_t)((int32_t)(st.keep << (31 - v)) >> 31);
