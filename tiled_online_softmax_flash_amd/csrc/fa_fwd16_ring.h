@@ -105,14 +105,24 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int LDW = TILE_BYTES / 1024 / DMA_WAVES;  // 1 KiB DMA ops per loading wave per operand per tile
     constexpr int NKS = DP / 16;                 // Q.K MFMAs per half-tile
     constexpr int NDB = DP / 32;                 // 32-dim output blocks
-    // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
-    // a step's mask values as well, and the head-dim-128 variants with a softcap or a scale
-    // multiply keep fewer too, so that no register spills (a spill copy of a register that an asm load has
-    // not filled yet would save stale data)
-    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? 6 : ((SOFTCAP != 0 || !RAW) && DP == 128 ? 10 : 12);
-    constexpr int NPRE = 4 * NDB < AHEAD ? 4 * NDB : AHEAD;   // V reads a block issues for the next one
     constexpr bool MASKED = MASKK != kMaskNone;
     constexpr bool SUB_FIRST = MASKED;
+    // head dim 64, masked: a step's mask values are loaded one step ahead.  With an fp32 mask
+    // they come through a per-wave LDS buffer filled by whole-line DMA: loading them straight
+    // into the lanes that use them makes every load touch 32 rows' cache lines, and those line
+    // lookups, not the bytes, bounded the kernel.
+    constexpr bool MASK_AHEAD = MASKED && DP == 64;
+    constexpr bool MASK_LDS = MASK_AHEAD && MASKK == kMaskF32 && RB == 1;
+    constexpr int MSK_WAVE = 2 * 32 * 128;   // one step's fp32 mask of a wave: 2 half-tiles x 32 rows x 128 B
+    // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
+    // a step's mask values as well, and the head-dim-128 variants with a softcap or a scale
+    // multiply, and the fp32-masked head-dim-64 ones with a softcap, keep fewer too, so that no
+    // register spills (a spill copy of a register that an asm load has
+    // not filled yet would save stale data)
+    constexpr int AHEAD = MASKK != kMaskNone && DP == 128 ? 6
+                        : (SOFTCAP != 0 || !RAW) && DP == 128 ? 10
+                        : MASK_LDS && SOFTCAP != 0 ? 10 : 12;
+    constexpr int NPRE = 4 * NDB < AHEAD ? 4 * NDB : AHEAD;   // V reads a block issues for the next one
     using MaskH = MaskHalf<MASKK>;
     static_assert(DP == 64 || DP == 128, "ring kernel covers head dims 64 and 128");
     static_assert(LDW >= 1 && LDW * DMA_WAVES * 1024 == TILE_BYTES, "tile must split evenly over the loading waves");
@@ -126,7 +136,9 @@ fwd16_ring_kernel(const FwdParams p) {
     constexpr int TBL_OFF = 2 * STAGES * TILE_BYTES;
     constexpr int STG_CHUNK = 32 * 8 + 32;
     constexpr int STG_OFF = TBL_OFF + WAVES * TBL_ROUNDS * 32;
-    __shared__ __attribute__((aligned(1024))) char lds[STG_OFF + WAVES * 8 * STG_CHUNK];
+    constexpr int MSK_OFF = STG_OFF + WAVES * 8 * STG_CHUNK;   // per-wave mask buffers (MASK_LDS)
+    static_assert(MSK_OFF % 128 == 0, "mask buffer rows must start on 128-byte boundaries");
+    __shared__ __attribute__((aligned(1024))) char lds[MSK_OFF + (MASK_LDS ? WAVES * MSK_WAVE : 0)];
     static_assert(sizeof(lds) <= 160 * 1024, "LDS budget of one workgroup");
     const uint32_t lds_base = lds_addr(lds);
 
@@ -163,6 +175,22 @@ fwd16_ring_kernel(const FwdParams p) {
             const int db = q / 128, key = 32 * hf + ((q >> 2) & 31), c = q & 3;
             v_src[j] = (uint32_t)(key * ROWB + (4 * db + c) * 16);
         }
+    }
+
+    // ---- mask buffer (MASK_LDS).  Half h of a wave's buffer holds 32 rows x 32 keys; row r is
+    // 128 bytes, its logical 16-byte chunk c (keys 4c .. 4c+3) stored at chunk c ^ (r % 8), so
+    // that the eight lanes of a 16-byte read cycle (rows r .. r+7, one chunk each) hit different
+    // banks.  DMA op j (0..7) fills half j / 4, rows 8 (j % 4) .. +7: lane l takes row
+    // 8 (j % 4) + l / 8, physical chunk l % 8.  msk_src: the lane's byte offset in the item's
+    // mask rows for ops with j % 4 = 0 (rows 8 further on for each step of j % 4; add the
+    // half-tile's key offset); msk_rd: LDS offset of lane (lr, hh)'s logical chunk 4 hh (chunk
+    // 4 hh + c is at msk_rd ^ 16 c).
+    uint32_t msk_src = 0, msk_rd = 0;
+    const uint32_t msk_row8 = (uint32_t)(8 * p.sk * 4);   // 8 mask rows in bytes
+    if constexpr (MASK_LDS) {
+        const int pr = lane >> 3, pc = lane & 7;
+        msk_src = (uint32_t)((int64_t)(wave * WROWS + pr) * p.sk * 4) + (uint32_t)(16 * (pc ^ pr));
+        msk_rd = (uint32_t)(MSK_OFF + wave * MSK_WAVE + lr * 128 + 16 * ((4 * hh) ^ (lr & 7)));
     }
 
     // ---- LDS operand addresses: one per-lane base per operand; ring slot, half-tile, K slice and
@@ -421,6 +449,26 @@ fwd16_ring_kernel(const FwdParams p) {
     auto launder_mask = [&](MaskH (&mh)[RB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) launder(mh[rb]);
+    };
+    // MASK_LDS: DMA of ring step s's mask (half-tiles 2s+1, 2s+2) into the wave's buffer, and
+    // the buffer's two halves into the lanes' mask registers
+    auto mask_dma = [&](int s) __attribute__((always_inline)) {
+        if constexpr (MASK_LDS) {
+            const uint32_t dst = lds_base + (uint32_t)(MSK_OFF + wave * MSK_WAVE);
+            static_for<0, 8>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                const uint32_t koff = (uint32_t)half_k0(2 * s + 1 + j / 4) * 4u + (uint32_t)(j % 4) * msk_row8;
+                dma_lds16(rmask, dst + 1024u * j, msk_src + koff);
+            });
+        }
+    };
+    auto mask_from_lds = [&](MaskH (&mh)[2][RB]) __attribute__((always_inline)) {
+        if constexpr (MASK_LDS) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mh[hf][0].w[c] = *(const u32x4*)(lds + (msk_rd ^ (16u * c)) + hf * (32 * 128));
+        }
     };
     auto mask_val = [&](const MaskH& mh, int v) __attribute__((always_inline)) -> float {
         if constexpr (MASKK == kMaskF32) {
@@ -849,7 +897,6 @@ fwd16_ring_kernel(const FwdParams p) {
     // pairs (2p, 2p+1) so that the mask buffers alternate statically; along p a wave's pairs
     // run skip, masked, full, masked, skip, each kind in a loop of its own (no branch on the
     // kind inside a loop, so the compiler keeps one register assignment per loop).
-    constexpr bool MASK_AHEAD = MASKED && DP == 64;
     f32x16 s_even[RB], s_odd[RB];
     u32x4 p_even[RB][2], p_odd[RB][2];
     u32x2 rpre[NPRE];   // leading V operand reads of the next block, issued by the block before
@@ -871,7 +918,13 @@ fwd16_ring_kernel(const FwdParams p) {
         // unmasked step -1: tiles 0 .. 2 are issued and tiles 0 and 1 landed and visible before
         // it, so it issues no loads and runs into step 0 without a wait or a barrier
         constexpr bool EARLY = PHASE == 0 && !MASKED;
-        if constexpr (MASK_AHEAD) {
+        if constexpr (MASK_LDS) {
+            // the buffer holds this step's successor's mask (DMA of two steps back): read it out,
+            // then refill the buffer with the mask of the step after that
+            mask_from_lds(mnext);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            mask_dma(t + 2);
+        } else if constexpr (MASK_AHEAD) {
             load_mask_half(2 * t + 3, mnext[0]);
             load_mask_half(2 * t + 4, mnext[1]);
         } else if constexpr (MASKED) {
@@ -977,6 +1030,7 @@ fwd16_ring_kernel(const FwdParams p) {
             f1 = __builtin_amdgcn_readfirstlane(f1);
         }
         if constexpr (MASK_AHEAD) load_mask_half(0, mask_b[1]);
+        mask_dma(0);   // (MASK_LDS) step 0's mask, read out by step -1
         if (!pre) {
             dma_issue_all(plan_tile(0));
             dma_issue_all(plan_tile(1));
