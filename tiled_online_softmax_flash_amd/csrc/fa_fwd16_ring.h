@@ -452,15 +452,16 @@ fwd16_ring_kernel(const FwdParams p) {
     };
     // MASK_LDS: DMA of ring step s's mask (half-tiles 2s+1, 2s+2) into the wave's buffer, and
     // the buffer's two halves into the lanes' mask registers
-    auto mask_dma = [&](int s) __attribute__((always_inline)) {
+    auto mask_dma_op = [&](int s, auto j_c) __attribute__((always_inline)) {
         if constexpr (MASK_LDS) {
+            constexpr int j = decltype(j_c)::value;
             const uint32_t dst = lds_base + (uint32_t)(MSK_OFF + wave * MSK_WAVE);
-            static_for<0, 8>([&](auto j_c) __attribute__((always_inline)) {
-                constexpr int j = decltype(j_c)::value;
-                const uint32_t koff = (uint32_t)half_k0(2 * s + 1 + j / 4) * 4u + (uint32_t)(j % 4) * msk_row8;
-                dma_lds16(rmask, dst + 1024u * j, msk_src + koff);
-            });
+            const uint32_t koff = (uint32_t)half_k0(2 * s + 1 + j / 4) * 4u + (uint32_t)(j % 4) * msk_row8;
+            dma_lds16(rmask, dst + 1024u * j, msk_src + koff);
         }
+    };
+    auto mask_dma = [&](int s) __attribute__((always_inline)) {
+        static_for<0, 8>([&](auto j_c) __attribute__((always_inline)) { mask_dma_op(s, j_c); });
     };
     auto mask_from_lds = [&](MaskH (&mh)[2][RB]) __attribute__((always_inline)) {
         if constexpr (MASK_LDS) {
@@ -921,9 +922,10 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (MASK_LDS) {
             // the buffer holds this step's successor's mask (DMA of two steps back): read it out,
             // then refill the buffer with the mask of the step after that
+            // (its refill is spread over the first block below, or issued here in a skip step)
             mask_from_lds(mnext);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            mask_dma(t + 2);
+            if constexpr (KIND == 0) mask_dma(t + 2);
         } else if constexpr (MASK_AHEAD) {
             load_mask_half(2 * t + 3, mnext[0]);
             load_mask_half(2 * t + 4, mnext[1]);
@@ -954,26 +956,44 @@ fwd16_ring_kernel(const FwdParams p) {
             const uint32_t v_slot = (uint32_t)((ring_base + t) & (STAGES - 1)) * TILE_BYTES;
             const uint32_t k_slot = (uint32_t)((ring_base + t + 1) & (STAGES - 1)) * TILE_BYTES;
             using F = bool_c<KIND == 2>;
-            // tile t+3's loads, spread evenly over the first block's MFMAs
-            auto spread = [&](auto m_c) __attribute__((always_inline)) {
+            // tile t+3's loads, spread evenly over the MFMAs of one block (MODE): the first block,
+            // or with MASK_LDS the second, the first then carrying the mask refill (the ring
+            // loads stay the step's most recent loads, which its closing wait leaves in flight)
+            auto spread_in = [&](auto mode_c, auto m_c) __attribute__((always_inline)) {
                 if constexpr (EARLY) return;
+                constexpr int MODE = decltype(mode_c)::value;
                 constexpr int m = decltype(m_c)::value;
-                constexpr int NMB = RB * (((MODE_A & kBlkPV) ? 2 * NDB : 0) + ((MODE_A & kBlkQK) ? NKS : 0));
+                constexpr int NMB = RB * (((MODE & kBlkPV) ? 2 * NDB : 0) + ((MODE & kBlkQK) ? NKS : 0));
                 static_assert(NMB >= NDMA, "one load per MFMA at most");
                 static_for<0, NDMA>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
                     if constexpr ((2 * i + 1) * NMB / (2 * NDMA) == m) dma_issue(dp, i_c);   // load i after MFMA m
                 });
             };
+            auto hook_a = [&](auto m_c) __attribute__((always_inline)) {
+                if constexpr (MASK_LDS) {
+                    constexpr int m = decltype(m_c)::value;
+                    constexpr int NMB = RB * (((MODE_A & kBlkPV) ? 2 * NDB : 0) + ((MODE_A & kBlkQK) ? NKS : 0));
+                    static_for<0, 8>([&](auto j_c) __attribute__((always_inline)) {
+                        constexpr int j = decltype(j_c)::value;
+                        if constexpr (j * NMB / 8 == m) mask_dma_op(t + 2, j_c);   // mask op j after MFMA m
+                    });
+                } else {
+                    spread_in(int_c<MODE_A>{}, m_c);
+                }
+            };
+            auto hook_b = [&](auto m_c) __attribute__((always_inline)) {
+                if constexpr (MASK_LDS) spread_in(int_c<MODE_B>{}, m_c);
+            };
             // The two waves of a SIMD run the same work; at equal priority the older one (waves
             // below WAVES / 2) wins the issue slots, runs ahead, and the younger one finishes
             // every step alone.  Raising the younger wave's priority for the first block lets
             // the pair finish a step together more closely.
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(1);
-            xbody(F{}, int_c<MODE_A>{}, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, spread);
+            xbody(F{}, int_c<MODE_A>{}, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, hook_a);
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(0);
             xbody(F{}, int_c<MODE_B>{}, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
-                  [](auto) {});
+                  hook_b);
         }
         if constexpr (!EARLY) {
             ring_wait();   // everything but tile t+3 landed
