@@ -13,13 +13,21 @@ struct DsaParams {
     const void* weights;   // [batch, q_seq, heads]
     const float* bias;     // [batch, 1, q_seq, key_seq]
     uint32_t* keys;        // workspace: [batch * q_seq, key_seq] order keys (0 = removed)
+    int* aux;              // workspace, after the keys: [batch * q_seq, kAuxInts] per-row words
+    int* counts;           // workspace, after aux: [batch * q_seq, chunks, 2] per-chunk counts
     int64_t* out;          // [batch, 1, q_seq, top_k]
     int64_t batch, q_seq, heads, head_dim, key_seq, top_k;
     float scale, weights_scale;
 };
 
+// Selection chunks and per-row workspace words (see dsa_select.hip): the workspace holds the
+// keys (4 bytes per cell), then kAuxInts words per row, then two words per chunk of
+// kSelChunkKeys positions of every row.
+constexpr int kAuxInts = 1028;
+constexpr int kSelChunkKeys = 2048;
+
 // dtype 0 f32, 1 f16, 2 bf16; head_dim <= 128.  Enqueues the scoring kernel (when key_seq > 0)
-// and the selection kernel (when there is a row).
+// and the selection kernels (when there is a row).
 hipError_t launch_index_select(const DsaParams& p, int dtype, hipStream_t s);
 
 }  // namespace dsa

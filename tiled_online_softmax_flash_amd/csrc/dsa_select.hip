@@ -1,7 +1,7 @@
 // Sparse index selection on gfx950: the operation of the onnx-runtime-ep-cuda page
 // `src/kernels/dsa_index_select.rs` (module documentation; "Determinism / bit-parity").
 //
-// Two kernels on the caller's stream:
+// Kernels on the caller's stream:
 //   * dsa_score_kernel: one thread per (query row, key position) cell.  It keeps its key row in
 //     registers as float32 and forms, for every head in ascending order, the dot product over
 //     the head dim in ascending order with every product and sum rounded on its own (no fused
@@ -12,13 +12,17 @@
 //     unsigned integer whose order is the IEEE-754 total order (never 0 for a canonical score).
 //     A workgroup covers 256 positions of one query row; the row's query is staged in LDS as
 //     float32 and read by broadcast loads.
-//   * dsa_select_kernel: one 1024-thread workgroup per query row, the row's keys cached in LDS
-//     (up to 32768 positions).  keep = min(#allowed, top_k).  The keep-th largest key is found
-//     exactly by four 8-bit radix passes (LDS histogram, block-wide descending prefix over the
-//     256 digits).  Positions are then compacted in ascending order, each thread owning a
-//     contiguous run of positions and two block prefix sums placing its winners: every key
-//     above the threshold, and the first keys equal to it, as many as the rank left over (ties
-//     go to the lower position).  The rest of the row is -1.
+//   * selection, in a row's chunks of 2048 positions, one 256-thread workgroup per chunk, so
+//     that a decode step's few rows still spread over the chip.  keep = min(#allowed, top_k).
+//     The keep-th largest key is found exactly by four 8-bit radix passes, one kernel each:
+//     every workgroup adds its chunk's histogram of the current digit (keys that match the
+//     digits found so far) into the row's histogram in the workspace, and the next pass's
+//     workgroups each read the finished histograms back to find the digits so far.  A count
+//     kernel then gives every chunk its keys above and equal to the threshold, and a write
+//     kernel places them: every key above the threshold, and the first keys equal to it, as
+//     many as the rank left over (ties go to the lower position), in ascending position order,
+//     each chunk's slots following from the counts of the chunks before it.  The rest of the
+//     row is -1.  The scoring kernel clears the row's histograms, so a call needs no memset.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
 #include <hip/hip_runtime.h>
 
@@ -29,7 +33,6 @@
 namespace dsa {
 
 constexpr int kScoreThreads = 256;
-constexpr int kSelectThreads = 1024;
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -66,6 +69,10 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
     const int64_t tiles = (p.key_seq + kScoreThreads - 1) / kScoreThreads;
     const int64_t row = (int64_t)blockIdx.x / tiles;
     const int64_t t = ((int64_t)blockIdx.x - row * tiles) * kScoreThreads + threadIdx.x;
+    // the row's selection histograms and counters start from zero (the first tile clears them;
+    // the selection kernels run after this kernel)
+    if ((int64_t)blockIdx.x == row * tiles)
+        for (int i = threadIdx.x; i < kAuxInts; i += kScoreThreads) p.aux[row * kAuxInts + i] = 0;
     const bool inside = t < p.key_seq;
     const int64_t cell = row * p.key_seq + (inside ? t : 0);
     const float bias = inside ? p.bias[cell] : 0.0f;
@@ -185,109 +192,203 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     return before + x;
 }
 
-// Rows of at most kKeyCache positions are read from the workspace once and kept in LDS for
-// the radix passes and the compaction, with one padding word after every 32 keys so that
-// threads walking contiguous 32-key runs hit distinct banks.
-constexpr int kKeyCache = 32768;
-__device__ __forceinline__ int64_t cache_index(int64_t t) { return t + (t >> 5); }
+// ---- selection, split over chunks of a row
+constexpr int kSelThreads = 256;
+constexpr int kSelChunk = kSelChunkKeys;          // positions per workgroup: 8 per thread
+constexpr int kKeysPerThread = kSelChunk / kSelThreads;
 
-template <bool CACHE>
-__global__ void __launch_bounds__(kSelectThreads) dsa_select_kernel(const DsaParams p) {
-    constexpr int NT = kSelectThreads;
-    __shared__ uint32_t kc[CACHE ? kKeyCache + kKeyCache / 32 : 1];
+// Per-row auxiliary words after the keys in the workspace (kAuxInts per row): the four passes'
+// histograms (256 each), then the allowed count, the threshold key, the ties to take, and one
+// spare.  Then per chunk of every row: its keys above and equal to the threshold.
+constexpr int kAuxHist = 0, kAuxAllowed = 1024, kAuxThr = 1025, kAuxTies = 1026;
+
+__host__ __device__ __forceinline__ int64_t sel_chunks(int64_t T) { return (T + kSelChunk - 1) / kSelChunk; }
+
+// The digit of the current pass that holds the rank-th largest key (rank >= 1, among the keys
+// that the histogram counts): the largest digit whose count of keys with this digit or a larger
+// one reaches rank.  *above gets the count of keys with a larger digit.  All 256 threads call it
+// (barriers); every thread gets the result.
+__device__ __forceinline__ int find_digit(const int* hist, int rank, int* wsum, int* pick, int* above) {
+    const int tid = threadIdx.x;
+    // thread i holds digit 255 - i: an inclusive prefix in thread order counts the keys with
+    // this digit or a larger one
+    const int cnt = hist[255 - tid];
+    int total;
+    const int cum = block_inclusive_sum<kSelThreads>(cnt, wsum, &total);
+    if (cum >= rank && cum - cnt < rank) {
+        pick[0] = 255 - tid;
+        pick[1] = cum - cnt;
+    }
+    __syncthreads();
+    const int digit = pick[0];
+    *above = pick[1];
+    __syncthreads();
+    return digit;
+}
+
+// Keys found so far: the digits of passes 0 .. npass-1 (in the high bits of *prefix) and the
+// rank left among the keys that match them.  Returns keep (0: nothing is selected).
+__device__ __forceinline__ int64_t sel_state(const DsaParams& p, const int* aux, int npass, uint32_t* prefix,
+                                             int* rank, int* wsum, int* pick) {
+    const int64_t allowed = aux[kAuxAllowed];
+    const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
+    *prefix = 0u;
+    *rank = (int)keep;
+    if (keep == 0) return 0;
+    for (int q = 0; q < npass; ++q) {
+        int above;
+        const int digit = find_digit(aux + kAuxHist + 256 * q, *rank, wsum, pick, &above);
+        *rank -= above;
+        *prefix |= (uint32_t)digit << (24 - 8 * q);
+    }
+    return keep;
+}
+
+// Radix pass PASS over one chunk: the chunk's histogram of digit PASS among the keys that match
+// the digits found so far, added into the row's histogram.  Pass 0 also counts the allowed
+// positions (keys of removed positions are 0, below every allowed key; keep <= #allowed, so they
+// never reach the threshold).
+template <int PASS>
+__global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p) {
     __shared__ int hist[256];
-    __shared__ int wsum[NT / 64];
+    __shared__ int wsum[kSelThreads / 64];
     __shared__ int pick[2];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
     const int64_t T = p.key_seq;
-    const uint32_t* gkeys = p.keys + row * T;
-    int64_t* out = p.out + row * p.top_k;
-    auto key_at = [&](int64_t t) -> uint32_t { return CACHE ? kc[cache_index(t)] : gkeys[t]; };
-
-    // allowed positions of the row (and the row into LDS)
-    int local = 0;
-#pragma unroll 4
-    for (int64_t t = tid; t < T; t += NT) {
-        const uint32_t k = gkeys[t];
-        if (CACHE) kc[cache_index(t)] = k;
-        local += k != 0u;
-    }
-    int n_allowed;
-    block_inclusive_sum<NT>(local, wsum, &n_allowed);   // its barriers also publish kc
-    const int64_t keep = (int64_t)n_allowed < p.top_k ? (int64_t)n_allowed : p.top_k;
-    for (int64_t s = keep + tid; s < p.top_k; s += NT) out[s] = -1;
-    if (keep == 0) return;
-
-    // the keep-th largest key: four passes over 8-bit digits, most significant first.  Keys of
-    // removed positions are 0, below every allowed key, and keep <= #allowed, so they never
-    // reach the threshold.
+    const int64_t nch = sel_chunks(T);
+    const int64_t row = (int64_t)blockIdx.x / nch;
+    const int64_t ch = (int64_t)blockIdx.x - row * nch;
+    int* aux = p.aux + row * kAuxInts;
+    const uint32_t* keys = p.keys + row * T;
     uint32_t prefix = 0u;
-    int rank = (int)keep;   // 1-based rank among the keys that match `prefix`, largest first
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-#pragma unroll 4
-        for (int64_t t = tid; t < T; t += NT) {
-            const uint32_t k = key_at(t);
+    int rank = 0;
+    if (PASS > 0 && sel_state(p, aux, PASS, &prefix, &rank, wsum, pick) == 0) return;
+    constexpr int shift = 24 - 8 * PASS;
+    constexpr uint32_t hi_mask = PASS == 0 ? 0u : (0xffffffffu << ((shift + 8) & 31));
+    hist[tid] = 0;
+    __syncthreads();
+    int allowed = 0;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
+        if (t < T) {
+            const uint32_t k = keys[t];
+            if (PASS == 0) allowed += k != 0u;
             if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
         }
-        __syncthreads();
-        // thread i < 256 holds digit 255 - i: an inclusive prefix in thread order is the count
-        // of keys with this digit or a larger one
-        const int cnt = tid < 256 ? hist[255 - tid] : 0;
-        int total;
-        const int cum = block_inclusive_sum<NT>(cnt, wsum, &total);
-        // exactly one digit (from the top) has a cumulative count that first reaches `rank`
-        // (the keys that match `prefix` number at least `rank`)
-        if (tid < 256 && cum >= rank && cum - cnt < rank) {
-            pick[0] = 255 - tid;
-            pick[1] = cum - cnt;   // keys with a larger digit
-        }
-        __syncthreads();
-        const uint32_t digit = (uint32_t)pick[0];
-        rank -= pick[1];
-        prefix |= digit << shift;
-        __syncthreads();
     }
-    const uint32_t thr = prefix;
-    const int ties_needed = rank;   // keys equal to the threshold to take, lowest positions first
+    __syncthreads();
+    if (hist[tid] != 0) atomicAdd(&aux[kAuxHist + 256 * PASS + tid], hist[tid]);
+    if (PASS == 0) {
+        int total;
+        block_inclusive_sum<kSelThreads>(allowed, wsum, &total);
+        if (tid == 0 && total != 0) atomicAdd(&aux[kAuxAllowed], total);
+    }
+}
 
-    // ascending compaction: thread i owns the contiguous positions [i C, (i + 1) C).  It counts
-    // its keys above and equal to the threshold; block prefix sums give it the ties it may take
-    // (the lowest positions first) and its first output slot; it then writes its winners in
-    // position order.
-    const int64_t C = (T + NT - 1) / NT;
-    const int64_t c0 = (int64_t)tid * C;
-    const int64_t c1 = c0 + C < T ? c0 + C : T;
+// The threshold (the keep-th largest key) and the ties to take from the four finished
+// histograms; each chunk's keys above and equal to it.
+__global__ void __launch_bounds__(kSelThreads) dsa_count_kernel(const DsaParams p) {
+    __shared__ int wsum[kSelThreads / 64];
+    __shared__ int pick[2];
+    const int tid = threadIdx.x;
+    const int64_t T = p.key_seq;
+    const int64_t nch = sel_chunks(T);
+    const int64_t row = (int64_t)blockIdx.x / nch;
+    const int64_t ch = (int64_t)blockIdx.x - row * nch;
+    int* aux = p.aux + row * kAuxInts;
+    const uint32_t* keys = p.keys + row * T;
+    uint32_t thr;
+    int ties;
+    if (sel_state(p, aux, 4, &thr, &ties, wsum, pick) == 0) return;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
+        if (t < T) {
+            const uint32_t k = keys[t];
+            gt += k > thr;
+            eq += k == thr;
+        }
+    }
+    int gt_all, eq_all;
+    block_inclusive_sum<kSelThreads>(gt, wsum, &gt_all);
+    block_inclusive_sum<kSelThreads>(eq, wsum, &eq_all);
+    if (tid == 0) {
+        p.counts[2 * (row * nch + ch)] = gt_all;
+        p.counts[2 * (row * nch + ch) + 1] = eq_all;
+        if (ch == 0) {
+            aux[kAuxThr] = (int)thr;
+            aux[kAuxTies] = ties;
+        }
+    }
+}
+
+// Output of one chunk: thread i owns positions [8 i, 8 i + 8) of the chunk.  The chunks before
+// it give the chunk's first output slot and the ties left for it; block prefix sums give each
+// thread the ties it may take (the lowest positions first) and its first slot; it writes its
+// winners in position order.  The slots past keep are -1 (spread over the row's chunks).
+__global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams p) {
+    __shared__ int wsum[kSelThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t T = p.key_seq;
+    const int64_t nch = sel_chunks(T);
+    const int64_t row = (int64_t)blockIdx.x / nch;
+    const int64_t ch = (int64_t)blockIdx.x - row * nch;
+    const int* aux = p.aux + row * kAuxInts;
+    const uint32_t* keys = p.keys + row * T;
+    int64_t* out = p.out + row * p.top_k;
+    const int64_t allowed = aux[kAuxAllowed];
+    const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
+    for (int64_t s = keep + ch * kSelThreads + tid; s < p.top_k; s += nch * kSelThreads) out[s] = -1;
+    if (keep == 0) return;
+    const uint32_t thr = (uint32_t)aux[kAuxThr];
+    const int ties_needed = aux[kAuxTies];
+    // keys above and equal to the threshold in the chunks before this one
+    int gt_b = 0, eq_b = 0;
+    for (int64_t c = tid; c < ch; c += kSelThreads) {
+        gt_b += p.counts[2 * (row * nch + c)];
+        eq_b += p.counts[2 * (row * nch + c) + 1];
+    }
+    int gt_before, eq_before;
+    block_inclusive_sum<kSelThreads>(gt_b, wsum, &gt_before);
+    block_inclusive_sum<kSelThreads>(eq_b, wsum, &eq_before);
+    const int ties_left = ties_needed - eq_before;   // ties this chunk and later ones may take
+    const int64_t slot0 = (int64_t)gt_before + (eq_before < ties_needed ? eq_before : ties_needed);
+    const int64_t t0 = ch * kSelChunk + (int64_t)tid * kKeysPerThread;
+    uint32_t k8[kKeysPerThread];
     int gt_n = 0, eq_n = 0;
-    for (int64_t t = c0; t < c1; ++t) {
-        const uint32_t k = key_at(t);
-        gt_n += k > thr;
-        eq_n += k == thr;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        k8[j] = t0 + j < T ? keys[t0 + j] : 0u;
+        gt_n += k8[j] > thr;
+        eq_n += k8[j] == thr;
     }
     int total;
-    const int eq_before = block_inclusive_sum<NT>(eq_n, wsum, &total) - eq_n;
-    int my_ties = ties_needed - eq_before;
+    const int eq_in = block_inclusive_sum<kSelThreads>(eq_n, wsum, &total) - eq_n;
+    int my_ties = ties_left - eq_in;
     my_ties = my_ties < 0 ? 0 : (my_ties > eq_n ? eq_n : my_ties);
     const int sel = gt_n + my_ties;
-    int64_t slot = block_inclusive_sum<NT>(sel, wsum, &total) - sel;
+    int64_t slot = slot0 + block_inclusive_sum<kSelThreads>(sel, wsum, &total) - sel;
     int ties_taken = 0;
-    for (int64_t t = c0; t < c1; ++t) {
-        const uint32_t k = key_at(t);
-        bool take = k > thr;
-        if (k == thr && ties_taken < my_ties) {
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        bool take = k8[j] > thr;
+        if (k8[j] == thr && ties_taken < my_ties) {
             take = true;
             ++ties_taken;
         }
         if (take) {
-            if (slot < keep) out[slot] = t;   // exactly keep are taken
+            if (slot < keep) out[slot] = t0 + j;   // exactly keep are taken
             ++slot;
         }
     }
+}
+
+// key_seq == 0: every row is -1.
+__global__ void __launch_bounds__(kSelThreads) dsa_fill_kernel(const DsaParams p) {
+    int64_t* out = p.out + (int64_t)blockIdx.x * p.top_k;
+    for (int64_t s = threadIdx.x; s < p.top_k; s += kSelThreads) out[s] = -1;
 }
 
 template <typename T>
@@ -306,15 +407,20 @@ hipError_t launch_score(const DsaParams& p, hipStream_t s) {
 hipError_t launch_index_select(const DsaParams& p, int dtype, hipStream_t s) {
     const int64_t rows = p.batch * p.q_seq;
     if (rows == 0) return hipSuccess;
-    if (p.key_seq > 0) {
-        hipError_t e = dtype == 0 ? launch_score<float>(p, s)
-                                  : (dtype == 1 ? launch_score<_Float16>(p, s) : launch_score<uint16_t>(p, s));
-        if (e != hipSuccess) return e;
+    if (p.key_seq == 0) {
+        hipLaunchKernelGGL(dsa_fill_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, s, p);
+        return hipGetLastError();
     }
-    if (p.key_seq <= kKeyCache)
-        hipLaunchKernelGGL(dsa_select_kernel<true>, dim3((unsigned)rows), dim3(kSelectThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(dsa_select_kernel<false>, dim3((unsigned)rows), dim3(kSelectThreads), 0, s, p);
+    hipError_t e = dtype == 0 ? launch_score<float>(p, s)
+                              : (dtype == 1 ? launch_score<_Float16>(p, s) : launch_score<uint16_t>(p, s));
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(rows * sel_chunks(p.key_seq)));
+    hipLaunchKernelGGL(dsa_pass_kernel<0>, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_pass_kernel<1>, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_pass_kernel<2>, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_pass_kernel<3>, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_count_kernel, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_write_kernel, grid, dim3(kSelThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -387,9 +387,16 @@ int flash_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, 
 
 size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq) {
     if (batch < 0 || q_seq < 0 || key_seq < 0) return 0;
-    int64_t bytes;
-    if (!count4(batch, q_seq, key_seq, 4, &bytes)) return 0;
-    return (size_t)bytes;
+    int64_t keys, rows;
+    if (!count4(batch, q_seq, key_seq, 4, &keys) || !count4(batch, q_seq, 1, 1, &rows)) return 0;
+    if (key_seq == 0 || rows == 0) return 0;
+    // keys, then per row kAuxInts words and two words per chunk of kSelChunkKeys positions
+    const int64_t chunks = ((int64_t)key_seq + dsa::kSelChunkKeys - 1) / dsa::kSelChunkKeys;
+    int64_t aux, cnt, total;
+    if (!mul_ok(rows, (int64_t)dsa::kAuxInts * 4, &aux) || !mul_ok(rows, chunks * 8, &cnt)) return 0;
+    total = keys + aux + cnt;
+    if (total < keys) return 0;
+    return (size_t)total;
 }
 
 int dsa_check_args(const void* query, const void* key, const void* weights, const float* bias,
@@ -428,7 +435,10 @@ int dsa_check_args(const void* query, const void* key, const void* weights, cons
         if (!mul_ok(rows, tiles, &grid) || grid > 0x7fffffffLL)
             return fail(FA_ERR_OVERFLOW, "scoring grid exceeds the launch limit");
     }
-    if (rows > 0x7fffffffLL) return fail(FA_ERR_OVERFLOW, "selection grid exceeds the launch limit");
+    int64_t sel_grid;
+    if (!mul_ok(rows, ((int64_t)key_seq + dsa::kSelChunkKeys - 1) / dsa::kSelChunkKeys, &sel_grid) ||
+        rows > 0x7fffffffLL || sel_grid > 0x7fffffffLL)
+        return fail(FA_ERR_OVERFLOW, "selection grid exceeds the launch limit");
     const size_t need = dsa_index_select_workspace_bytes(batch, q_seq, key_seq);
     if (need > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
         return fail(FA_ERR_INVALID_ARGUMENT, "the index selection needs a 16-byte aligned workspace of %zu bytes "
@@ -449,6 +459,8 @@ int dsa_index_select(const void* query, const void* key, const void* weights, co
     p.weights = weights;
     p.bias = bias;
     p.keys = (uint32_t*)workspace;
+    p.aux = (int*)((char*)workspace + (size_t)batch * q_seq * key_seq * 4);
+    p.counts = p.aux + (size_t)batch * q_seq * dsa::kAuxInts;
     p.out = out;
     p.batch = batch;
     p.q_seq = q_seq;
