@@ -46,7 +46,7 @@ PEAK_EXP_PER_S = 256 * 4 * 16 * 2.4e9 / 2
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk_eff·D) + % of MI355X MFMA peak"
 KERNEL_SOURCES = ["fa_device.h", "fa_params.h", "fa_fwd16.h", "fa_fwd16_ring.h",
                   "fa_fwd16_ring_consts.h", "fa_fwd32.h", "fa_fwd32w.h", "fa_splitkv.h",
-                  "fa_launch.h", "fa_api.hip"]
+                  "fa_launch.h", "fa_api.hip", "dsa_select.hip", "dsa_kernels.h"]
 
 
 def kernel_hash() -> str:

@@ -71,7 +71,7 @@ int dsa_check_args(const void* query, const void* key, const void* weights, cons
                    size_t workspace_bytes);
 
 /* Workspace bytes dsa_index_select needs: 4 per (batch, query row, key position) cell (the
- * cells' order keys, first), then for every query row 4112 bytes of radix histograms and
+ * cells' order keys, first), then for every query row 20496 bytes of radix histograms and
  * counters and 8 bytes per 2048 key positions; 0 when key_seq or batch * q_seq is 0, for
  * negative sizes or on overflow.  Host only. */
 size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq);

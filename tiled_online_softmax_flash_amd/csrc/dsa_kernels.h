@@ -23,7 +23,7 @@ struct DsaParams {
 // Selection chunks and per-row workspace words (see dsa_select.hip): the workspace holds the
 // keys (4 bytes per cell), then kAuxInts words per row, then two words per chunk of
 // kSelChunkKeys positions of every row.
-constexpr int kAuxInts = 1028;
+constexpr int kAuxInts = 5124;
 constexpr int kSelChunkKeys = 2048;
 
 // dtype 0 f32, 1 f16, 2 bf16; head_dim <= 128.  Enqueues the scoring kernel (when key_seq > 0)

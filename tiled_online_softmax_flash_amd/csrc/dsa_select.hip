@@ -14,7 +14,8 @@
 //     float32 and read by broadcast loads.
 //   * selection, in a row's chunks of 2048 positions, one 256-thread workgroup per chunk, so
 //     that a decode step's few rows still spread over the chip.  keep = min(#allowed, top_k).
-//     The keep-th largest key is found exactly by four 8-bit radix passes, one kernel each:
+//     The keep-th largest key is found exactly by three radix passes (digits of 11, 11 and 10
+//     bits), one kernel each:
 //     every workgroup adds its chunk's histogram of the current digit (keys that match the
 //     digits found so far) into the row's histogram in the workspace, and the next pass's
 //     workgroups each read the finished histograms back to find the digits so far.  A count
@@ -197,27 +198,49 @@ constexpr int kSelThreads = 256;
 constexpr int kSelChunk = kSelChunkKeys;          // positions per workgroup: 8 per thread
 constexpr int kKeysPerThread = kSelChunk / kSelThreads;
 
-// Per-row auxiliary words after the keys in the workspace (kAuxInts per row): the four passes'
-// histograms (256 each), then the allowed count, the threshold key, the ties to take, and one
-// spare.  Then per chunk of every row: its keys above and equal to the threshold.
-constexpr int kAuxHist = 0, kAuxAllowed = 1024, kAuxThr = 1025, kAuxTies = 1026;
+// The key is found in three radix passes over digits of 11, 11 and 10 bits (most significant
+// first).  Per-row auxiliary words after the keys in the workspace (kAuxInts per row): the three
+// passes' histograms (2048, 2048 and 1024 words), then the allowed count, the threshold key and
+// the ties to take.  Then per chunk of every row: its keys above and equal to the threshold.
+constexpr int kPasses = 3;
+constexpr int kMaxBins = 2048;
+__host__ __device__ constexpr int pass_bits(int q) { return q < 2 ? 11 : 10; }
+__host__ __device__ constexpr int pass_shift(int q) { return q == 0 ? 21 : (q == 1 ? 10 : 0); }
+__host__ __device__ constexpr int pass_hist(int q) { return q == 0 ? 0 : (q == 1 ? 2048 : 4096); }
+constexpr int kAuxAllowed = 5120, kAuxThr = 5121, kAuxTies = 5122;
+static_assert(kAuxTies < kAuxInts, "per-row words");
 
 __host__ __device__ __forceinline__ int64_t sel_chunks(int64_t T) { return (T + kSelChunk - 1) / kSelChunk; }
 
-// The digit of the current pass that holds the rank-th largest key (rank >= 1, among the keys
-// that the histogram counts): the largest digit whose count of keys with this digit or a larger
-// one reaches rank.  *above gets the count of keys with a larger digit.  All 256 threads call it
-// (barriers); every thread gets the result.
-__device__ __forceinline__ int find_digit(const int* hist, int rank, int* wsum, int* pick, int* above) {
+// The digit of pass q that holds the rank-th largest key (rank >= 1, among the keys that the
+// histogram counts): the largest digit whose count of keys with this digit or a larger one
+// reaches rank.  *above gets the count of keys with a larger digit.  Thread i sums digits
+// nb-1-DPT*i down to nb-DPT*(i+1); a prefix over the threads finds the thread whose run holds
+// the crossing, which walks its digits.  All 256 threads call it (barriers); every thread gets
+// the result.
+__device__ __forceinline__ int find_digit(const int* hist, int nb, int rank, int* wsum, int* pick, int* above) {
     const int tid = threadIdx.x;
-    // thread i holds digit 255 - i: an inclusive prefix in thread order counts the keys with
-    // this digit or a larger one
-    const int cnt = hist[255 - tid];
+    const int dpt = nb / kSelThreads;
+    const int hi = nb - 1 - dpt * tid;
+    int c[kMaxBins / kSelThreads];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kSelThreads; ++j) {
+        c[j] = j < dpt ? hist[hi - j] : 0;
+        cnt += c[j];
+    }
     int total;
     const int cum = block_inclusive_sum<kSelThreads>(cnt, wsum, &total);
     if (cum >= rank && cum - cnt < rank) {
-        pick[0] = 255 - tid;
-        pick[1] = cum - cnt;
+        int run = cum - cnt;
+#pragma unroll
+        for (int j = 0; j < kMaxBins / kSelThreads; ++j) {
+            if (j < dpt && run < rank && run + c[j] >= rank) {
+                pick[0] = hi - j;
+                pick[1] = run;
+            }
+            run += c[j];
+        }
     }
     __syncthreads();
     const int digit = pick[0];
@@ -226,8 +249,8 @@ __device__ __forceinline__ int find_digit(const int* hist, int rank, int* wsum, 
     return digit;
 }
 
-// Keys found so far: the digits of passes 0 .. npass-1 (in the high bits of *prefix) and the
-// rank left among the keys that match them.  Returns keep (0: nothing is selected).
+// Keys found so far: the digits of passes 0 .. npass-1 (in their bits of *prefix) and the rank
+// left among the keys that match them.  Returns keep (0: nothing is selected).
 __device__ __forceinline__ int64_t sel_state(const DsaParams& p, const int* aux, int npass, uint32_t* prefix,
                                              int* rank, int* wsum, int* pick) {
     const int64_t allowed = aux[kAuxAllowed];
@@ -237,9 +260,9 @@ __device__ __forceinline__ int64_t sel_state(const DsaParams& p, const int* aux,
     if (keep == 0) return 0;
     for (int q = 0; q < npass; ++q) {
         int above;
-        const int digit = find_digit(aux + kAuxHist + 256 * q, *rank, wsum, pick, &above);
+        const int digit = find_digit(aux + pass_hist(q), 1 << pass_bits(q), *rank, wsum, pick, &above);
         *rank -= above;
-        *prefix |= (uint32_t)digit << (24 - 8 * q);
+        *prefix |= (uint32_t)digit << pass_shift(q);
     }
     return keep;
 }
@@ -250,7 +273,10 @@ __device__ __forceinline__ int64_t sel_state(const DsaParams& p, const int* aux,
 // never reach the threshold).
 template <int PASS>
 __global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p) {
-    __shared__ int hist[256];
+    constexpr int NB = 1 << pass_bits(PASS);
+    constexpr int shift = pass_shift(PASS);
+    constexpr uint32_t hi_mask = PASS == 0 ? 0u : (0xffffffffu << ((shift + pass_bits(PASS)) & 31));
+    __shared__ int hist[NB];
     __shared__ int wsum[kSelThreads / 64];
     __shared__ int pick[2];
     const int tid = threadIdx.x;
@@ -260,25 +286,32 @@ __global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p
     const int64_t ch = (int64_t)blockIdx.x - row * nch;
     int* aux = p.aux + row * kAuxInts;
     const uint32_t* keys = p.keys + row * T;
+    // the chunk's keys are requested first, so that their latency overlaps the histogram reads
+    uint32_t kk[kKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
+        kk[j] = t < T ? keys[t] : 0u;
+    }
     uint32_t prefix = 0u;
     int rank = 0;
     if (PASS > 0 && sel_state(p, aux, PASS, &prefix, &rank, wsum, pick) == 0) return;
-    constexpr int shift = 24 - 8 * PASS;
-    constexpr uint32_t hi_mask = PASS == 0 ? 0u : (0xffffffffu << ((shift + 8) & 31));
-    hist[tid] = 0;
+#pragma unroll
+    for (int i = tid; i < NB; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     int allowed = 0;
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
-        const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
-        if (t < T) {
-            const uint32_t k = keys[t];
+        if (ch * kSelChunk + j * kSelThreads + tid < T) {
+            const uint32_t k = kk[j];
             if (PASS == 0) allowed += k != 0u;
-            if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+            if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(NB - 1)], 1);
         }
     }
     __syncthreads();
-    if (hist[tid] != 0) atomicAdd(&aux[kAuxHist + 256 * PASS + tid], hist[tid]);
+#pragma unroll
+    for (int i = tid; i < NB; i += kSelThreads)
+        if (hist[i] != 0) atomicAdd(&aux[pass_hist(PASS) + i], hist[i]);
     if (PASS == 0) {
         int total;
         block_inclusive_sum<kSelThreads>(allowed, wsum, &total);
@@ -286,7 +319,7 @@ __global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p
     }
 }
 
-// The threshold (the keep-th largest key) and the ties to take from the four finished
+// The threshold (the keep-th largest key) and the ties to take from the three finished
 // histograms; each chunk's keys above and equal to it.
 __global__ void __launch_bounds__(kSelThreads) dsa_count_kernel(const DsaParams p) {
     __shared__ int wsum[kSelThreads / 64];
@@ -298,18 +331,21 @@ __global__ void __launch_bounds__(kSelThreads) dsa_count_kernel(const DsaParams 
     const int64_t ch = (int64_t)blockIdx.x - row * nch;
     int* aux = p.aux + row * kAuxInts;
     const uint32_t* keys = p.keys + row * T;
-    uint32_t thr;
-    int ties;
-    if (sel_state(p, aux, 4, &thr, &ties, wsum, pick) == 0) return;
-    int gt = 0, eq = 0;
+    uint32_t kk[kKeysPerThread];   // requested before the histograms are read
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
         const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
-        if (t < T) {
-            const uint32_t k = keys[t];
-            gt += k > thr;
-            eq += k == thr;
-        }
+        kk[j] = t < T ? keys[t] : 0u;
+    }
+    uint32_t thr;
+    int ties;
+    if (sel_state(p, aux, kPasses, &thr, &ties, wsum, pick) == 0) return;
+    // (positions past T hold 0 here, which is below the threshold, an allowed key)
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        gt += kk[j] > thr;
+        eq += kk[j] == thr;
     }
     int gt_all, eq_all;
     block_inclusive_sum<kSelThreads>(gt, wsum, &gt_all);
@@ -338,6 +374,11 @@ __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams 
     const int* aux = p.aux + row * kAuxInts;
     const uint32_t* keys = p.keys + row * T;
     int64_t* out = p.out + row * p.top_k;
+    // the chunk's keys are requested before the row's words and counts are read
+    const int64_t t0 = ch * kSelChunk + (int64_t)tid * kKeysPerThread;
+    uint32_t k8[kKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) k8[j] = t0 + j < T ? keys[t0 + j] : 0u;
     const int64_t allowed = aux[kAuxAllowed];
     const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
     for (int64_t s = keep + ch * kSelThreads + tid; s < p.top_k; s += nch * kSelThreads) out[s] = -1;
@@ -355,12 +396,9 @@ __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams 
     block_inclusive_sum<kSelThreads>(eq_b, wsum, &eq_before);
     const int ties_left = ties_needed - eq_before;   // ties this chunk and later ones may take
     const int64_t slot0 = (int64_t)gt_before + (eq_before < ties_needed ? eq_before : ties_needed);
-    const int64_t t0 = ch * kSelChunk + (int64_t)tid * kKeysPerThread;
-    uint32_t k8[kKeysPerThread];
     int gt_n = 0, eq_n = 0;
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
-        k8[j] = t0 + j < T ? keys[t0 + j] : 0u;
         gt_n += k8[j] > thr;
         eq_n += k8[j] == thr;
     }
@@ -415,10 +453,10 @@ hipError_t launch_index_select(const DsaParams& p, int dtype, hipStream_t s) {
                               : (dtype == 1 ? launch_score<_Float16>(p, s) : launch_score<uint16_t>(p, s));
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(rows * sel_chunks(p.key_seq)));
+    static_assert(kPasses == 3, "one launch per pass");
     hipLaunchKernelGGL(dsa_pass_kernel<0>, grid, dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(dsa_pass_kernel<1>, grid, dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(dsa_pass_kernel<2>, grid, dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL(dsa_pass_kernel<3>, grid, dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(dsa_count_kernel, grid, dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(dsa_write_kernel, grid, dim3(kSelThreads), 0, s, p);
     return hipGetLastError();
