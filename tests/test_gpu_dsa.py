@@ -45,6 +45,14 @@ CASES = {
     "bf16_uncached_long": dict(seed=90, batch=1, q_seq=2, heads=2, head_dim=32, key_seq=40000,
                                top_k=1000, dtype="bf16", bias="random", hole_p=0.1),
     # many rows and a long key range
+    # ties at the threshold spread over several 2048-position chunks of a row (integer inputs:
+    # a handful of distinct scores), and a multi-chunk row with fewer allowed positions than
+    # top_k (-1 padding after winners from every chunk)
+    "bf16_ties_many_chunks": dict(seed=92, batch=2, q_seq=2, heads=2, head_dim=8, key_seq=9000,
+                                  top_k=3000, dtype="bf16", bias="zero", int_values=True,
+                                  scale=1.0),
+    "f16_multichunk_padding": dict(seed=93, batch=1, q_seq=3, heads=4, head_dim=16, key_seq=5000,
+                                   top_k=4500, dtype="f16", bias="random", hole_p=0.2),
     "bf16_rows_long": dict(seed=88, batch=2, q_seq=5, heads=16, head_dim=128, key_seq=8192,
                            top_k=2048, dtype="bf16"),
 }
