@@ -37,18 +37,15 @@ __device__ __forceinline__ float tanh_fast(float y) {
     return __builtin_fabsf(y) < 0.125f ? small : big;
 }
 
-// tanh(y) from the identity tanh y = 1 - 2 / (e^{2y} + 1) alone: absolute error a few fp32 ulps
-// of 1 everywhere (it saturates cleanly to +-1), but no relative accuracy near 0.  Scaled by a
-// softcap c <= kTanhIdentityMaxCap the capped score is off by at most about c * 2^-21 < 5e-4,
-// which leaves the softmax weights within 1e-3 relative; larger caps use tanh_fast.
+// The identity tanh y = 1 - 2 / (e^{2y} + 1) alone (tanh_identity_z below) has an absolute
+// error of a few fp32 ulps of 1 everywhere (it saturates cleanly to +-1), but no relative
+// accuracy near 0.  Scaled by a softcap c <= kTanhIdentityMaxCap the capped score is off by at
+// most about c * 2^-21 < 5e-4, which leaves the softmax weights within 1e-3 relative; larger caps
+// use tanh_fast.
 constexpr float kTanhIdentityMaxCap = 1024.0f;
-__device__ __forceinline__ float tanh_identity(float y) {
-    const float e = exp2_hw(y * (2.0f * kLog2e));
-    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-}
 
 // tanh in terms of z = 2 log2(e) y (the argument of the identity's exponential).
-//   tanh_identity_z: 1 - 2 / (2^z + 1), one exponential and one reciprocal (see tanh_identity).
+//   tanh_identity_z: 1 - 2 / (2^z + 1), one exponential and one reciprocal (accuracy above).
 //   tanh_series_z, for |y| < 1/8 (|z| < kTanhSeriesMaxZ): the odd series y - y^3/3 + 2 y^5/15
 //   written in z, no transcendental instruction.  Its truncation error is below
 //   (17/315) y^7 <= 2.1e-7 |y| there, under the identity's absolute error of a few ulps of 1.
