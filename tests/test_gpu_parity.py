@@ -146,6 +146,14 @@ EDGE = {
                                    softcap=3.0),
     "fp32_d129_token_major": dict(seed=53, batch=2, heads=3, kv_heads=3, sq=65, sk=65, dim=129,
                                   dtype="f32", out_layout="token"),
+    # wide fp32 head dims on whole 64-dim runs below 384 (the K dims past them are never loaded)
+    # and a 16-dim-aligned one, with an additive mask and no softcap
+    "fp32_d256_mask": dict(seed=91, batch=1, heads=3, kv_heads=1, sq=90, sk=150, dim=256,
+                           dtype="f32", mask="bernoulli", mask_p=0.3, dead_rows=2),
+    "fp32_d192_causal_ragged": dict(seed=92, batch=2, heads=2, kv_heads=1, sq=97, sk=131, dim=192,
+                                    dtype="f32", causal=True),
+    "fp32_d336_long": dict(seed=93, batch=1, heads=1, kv_heads=1, sq=64, sk=700, dim=336,
+                           dtype="f32"),
     # scores that drift by hundreds along the keys (rising for some rows, falling for others):
     # later half-tiles exceed the running maximum far beyond the lazy-rescale bound, and their
     # weights against the old maximum overflow fp32 (head dims 128 and 64, with and without a

@@ -202,6 +202,16 @@ __device__ __forceinline__ void dma_lds16(u32x4 rsrc, uint32_t lds_addr, uint32_
                  : "m0");
 }
 
+// 4-byte buffer load straight into LDS: lane l's dword (from byte voffset + soffset of the
+// buffer described by `rsrc`) lands at LDS byte address `lds_addr + 4 * l`.  A lane whose
+// voffset lies past the buffer's size writes 0.
+__device__ __forceinline__ void dma_lds4(u32x4 rsrc, uint32_t lds_addr, uint32_t voffset, uint32_t soffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight (loads retire in
 // order; stores count too).
 template <int N>

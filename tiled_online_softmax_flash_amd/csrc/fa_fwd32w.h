@@ -3,16 +3,19 @@
 // The pictor-kernels page (`src/gpu_backend/cuda_imagen_attn_kernels.rs`) builds its fp32
 // joint-attention kernel a second time with a head-dim bound of 384, for the image decoder's
 // attention (96 KiB of K/V per block there).  Same method and fp32 arithmetic as fa_fwd32.h
-// (v_mfma_f32_32x32x2_f32 products, fp32 accumulation, no reduced-precision staging of Q, K, V,
-// S or P); the head dim is split into three 128-dim groups so that each wave keeps the registers
-// of a 128-dim kernel:
-//   * 6 waves: row block rb (32 query rows; 2 per workgroup) x dim group g (128 dims).
-//   * A 32-key K/V tile of all 384 dims sits in LDS (K row-permuted, V transposed; 105 KB),
-//     single-buffered: at these head dims the products cost many times the tile load.
-//   * Wave (rb, g) takes the scores' partial sums over its dims, S_g = K_g Q_g^T.  The three
+// (full fp32 products on v_mfma_f32_32x32x2_f32, fp32 accumulation, no reduced-precision
+// staging of Q, K, V, S or P); the head dim is split into four 96-dim groups so that each wave
+// keeps few registers:
+//   * 8 waves: row block rb (32 query rows; 2 per workgroup) x dim group g (96 dims), two waves
+//     per SIMD (with three groups, six waves left two SIMDs with one wave and two with two).
+//   * A 32-key K/V tile of all 384 dims sits in LDS (K row-permuted, V as [key quad][dim][4
+//     keys]; 97 KB), single-buffered, filled by buffer-to-LDS loads that run under the other
+//     half of the tile's work: the next K tile under the softmax and P.V, the next V tile under
+//     the next Q.K.  Two barriers a tile.
+//   * Wave (rb, g) takes the scores' partial sums over its dims, S_g = K_g Q_g^T.  The four
 //     partials of a row block meet in LDS and every wave of the row block adds them in the
-//     order g = 0, 1, 2, so the three hold identical scores and run an identical softmax; each
-//     then adds P V_g to its own 128 dims of O.
+//     order g = 0, 1, 2, 3, so the four hold identical scores and run an identical softmax; each
+//     then adds P V_g to its own 96 dims of O.
 #pragma once
 
 #include "fa_device.h"
@@ -22,20 +25,17 @@ namespace fa {
 template <bool MASKED, bool SOFTCAP, bool RAW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads)))
 fwd32w_kernel(const FwdParams p) {
-    constexpr int DP = 384, GD = 128, NG = 3, RBW = kWideRows / kWaveRows, BN = 32, NT = kWideThreads;
+    constexpr int DP = 384, GD = 96, NG = 4, RBW = kWideRows / kWaveRows, BN = 32, NT = kWideThreads;
     constexpr int KP = DP + 4;          // K tile row pitch (floats): 16-byte pad
-    constexpr int VP = BN + 4;          // V^T tile row pitch (floats): 16-byte pad
+    constexpr int VQ = DP * 4;          // floats of one key quad of the V tile ([dim][4 keys])
     constexpr int KSZ = BN * KP;
-    constexpr int VSZ = DP * VP;
+    constexpr int VSZ = (BN / 4) * VQ;
     constexpr int NQC = GD / 8;         // 8-dim chunks of a group's part of the QK reduction
     constexpr int NDB = GD / 32;        // 32-dim output blocks of a group
-    constexpr int CPR = DP / 4;         // 16-byte chunks per K row
-    constexpr int NKC = BN * CPR / NT;
-    constexpr int NVBLK = (BN / 4) * (DP / 4);
-    constexpr int NVB = NVBLK / NT;
     constexpr int SPART = 64 * 16;      // floats of one wave's partial scores
     static_assert(RBW * NG * 64 == NT, "one wave per (row block, dim group)");
-    static_assert(NKC * NT == BN * CPR && NVB * NT == NVBLK, "tile loads split evenly");
+    static_assert(NT / 64 * 4 == BN, "each wave loads four keys of a tile");
+    static_assert(GD % 32 == 0 && GD * NG == DP, "dim groups of whole 32-dim blocks");
 
     __shared__ __attribute__((aligned(16))) float lds[KSZ + VSZ + RBW * NG * SPART];
     float* const kl = lds;
@@ -108,66 +108,71 @@ fwd32w_kernel(const FwdParams p) {
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
 
-    // K/V tile kt into LDS by all threads (rows past the cache length as zeros); K, then V, so
-    // that only one of them is held in registers at a time
-    auto stage_tile = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * BN;
-        {
-            f32x4 kreg[NKC];
+    // K/V tile kt into LDS by buffer-to-LDS loads (4 bytes a lane, 256 bytes an instruction), no
+    // registers in between.  Wave w loads keys 4w..4w+3 of the tile: K in 64-dim runs of one key,
+    // V in 16-dim x 4-key blocks (lane l: key 4w + l%4, dim 16m + l/4), which puts V in LDS as
+    // [key quad][dim][4 keys].  Rows past the cache length read as zeros (the tile's buffer ends
+    // at the last valid row); lanes past the head dim take an offset past any buffer (zeros).
+    const int kfull = D >> 6, vfull = D >> 4;           // whole 64-dim K runs, 16-dim V blocks
+    const bool kpart = (D & 63) != 0, vpart = (D & 15) != 0;
+    uint32_t kvo[4], kvo_p[4];
 #pragma unroll
-            for (int n = 0; n < NKC; ++n) {
-                const int c = tid + NT * n;
-                const int krow = c / CPR;
-                const int kcol = (c % CPR) * 4;
-                const int64_t j = k0 + krow;
-                f32x4 val = f32x4(0.0f);
-                if (j < rule.L && kcol < D) {
-                    const float* src = kg + j * D + kcol;
-                    if (p.vec_kv) {
-                        val = *(const f32x4*)src;
-                    } else {
+    for (int i = 0; i < 4; ++i) {
+        kvo[i] = (uint32_t)(((4 * wave + i) * D + lane) * 4);
+        kvo_p[i] = lane < D - 64 * kfull ? kvo[i] : kOutOfRange;
+    }
+    const uint32_t vvo = (uint32_t)(((4 * wave + (lane & 3)) * D + (lane >> 2)) * 4);
+    const uint32_t vvo_p = 16 * vfull + (lane >> 2) < D ? vvo : kOutOfRange;
+    const uint32_t kl_base = lds_addr(kl), vl_base = lds_addr(vl) + (uint32_t)(wave * VQ * 4);
+    auto tile_rows = [&](int kt) -> int {
+        const int64_t left = rule.L - (int64_t)kt * BN;
+        return left >= BN ? BN : left > 0 ? (int)left : 0;
+    };
+    // Head dim 384 (every run and block whole) issues straight-line code; other head dims loop.
+    auto issue_k = [&](int kt) {
+        const u32x4 rk = make_rsrc_words(kg + (int64_t)kt * BN * D, tile_rows(kt) * D * 4);
+        // opaque copy: the LDS addresses are formed here, per tile, instead of being hoisted out
+        // of the tile loop into scalar registers (which then spill)
+        uint32_t kb = kl_base;
+        asm volatile("" : "+s"(kb));
+        if (kfull == DP / 64) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (kcol + e < D) val[e] = src[e];
-                    }
-                }
-                kreg[n] = val;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t dst = kb + (uint32_t)(lds_row_of_key(4 * wave + i) * KP * 4);
+#pragma unroll
+                for (int c = 0; c < DP / 64; ++c) dma_lds4(rk, dst + 256 * c, kvo[i], 256 * c);
             }
+        } else {
 #pragma unroll
-            for (int n = 0; n < NKC; ++n) {
-                const int c = tid + NT * n;
-                const int krow = c / CPR;
-                const int kcol = (c % CPR) * 4;
-                *(f32x4*)(kl + lds_row_of_key(krow) * KP + kcol) = kreg[n];
+            for (int i = 0; i < 4; ++i) {
+                uint32_t dst = kb + (uint32_t)(lds_row_of_key(4 * wave + i) * KP * 4);
+                uint32_t so = 0;
+#pragma unroll 1
+                for (int c = 0; c < kfull; ++c, dst += 256, so += 256) dma_lds4(rk, dst, kvo[i], so);
+                if (kpart) dma_lds4(rk, dst, kvo_p[i], so);
             }
-        }
-#pragma unroll
-        for (int n = 0; n < NVB; ++n) {
-            const int blk = tid + NT * n;
-            const int kq = blk & 7;
-            const int dq = blk >> 3;
-            f32x4 vreg[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t j = k0 + 4 * kq + e;
-                f32x4 val = f32x4(0.0f);
-                if (j < rule.L && 4 * dq < D) {
-                    const float* src = vg + j * D + 4 * dq;
-                    if (p.vec_kv) {
-                        val = *(const f32x4*)src;
-                    } else {
-#pragma unroll
-                        for (int x = 0; x < 4; ++x)
-                            if (4 * dq + x < D) val[x] = src[x];
-                    }
-                }
-                vreg[e] = val;
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                *(f32x4*)(vl + (4 * dq + c) * VP + 4 * kq) = f32x4{vreg[0][c], vreg[1][c], vreg[2][c], vreg[3][c]};
         }
     };
+    auto issue_v = [&](int kt) {
+        const u32x4 rv = make_rsrc_words(vg + (int64_t)kt * BN * D, tile_rows(kt) * D * 4);
+        uint32_t vb = vl_base;
+        asm volatile("" : "+s"(vb));
+        if (vfull == DP / 16) {
+#pragma unroll
+            for (int m = 0; m < DP / 16; ++m) dma_lds4(rv, vb + 256 * m, vvo, 64 * m);
+        } else {
+            uint32_t so = 0;
+#pragma unroll 1
+            for (int m = 0; m < vfull; ++m, vb += 256, so += 64) dma_lds4(rv, vb, vvo, so);
+            if (vpart) dma_lds4(rv, vb, vvo_p, so);
+        }
+    };
+    // K dims past the last 64-dim run are never loaded: zero them once (Q is zero there too)
+    {
+        const int z0 = 64 * (kfull + (kpart ? 1 : 0));
+        const int zw = DP - z0;
+        for (int idx = tid; idx < BN * zw; idx += NT) kl[(idx / zw) * KP + z0 + idx % zw] = 0.0f;
+    }
 
     auto epi = [&](float sv, float mv) -> float {
         if constexpr (SOFTCAP) {
@@ -181,14 +186,19 @@ fwd32w_kernel(const FwdParams p) {
     };
 
     float* const my_part = part + (rbw * NG + g) * SPART;
+    if (n_tiles > 0) {
+        issue_k(kt_begin);
+        issue_v(kt_begin);
+        dma_wait<0>();
+    }
+    __syncthreads();   // tile 0 and the zeroed K dims visible to every wave
     for (int t = 0; t < n_tiles; ++t) {
         const int kt = kt_begin + t;
         const int64_t k0 = (int64_t)kt * BN;
         const int64_t k1 = k0 + BN - 1;
-        // the three waves of a row block decide alike; every wave reaches every barrier
+        const bool more = t + 1 < n_tiles;
+        // the four waves of a row block decide alike; every wave reaches every barrier
         const bool act = wave_has_rows && !(k0 > w_hi_max || k1 < w_lo_min || w_lo_min > w_hi_max);
-        stage_tile(kt);
-        __syncthreads();
         if (act) {
             // partial S^T = K_g Q_g^T over this group's dims
             f32x16 s = f32x16(0.0f);
@@ -203,7 +213,9 @@ fwd32w_kernel(const FwdParams p) {
             for (int c = 0; c < 4; ++c)
                 *(f32x4*)(my_part + (c * 64 + lane) * 4) = f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
         }
-        __syncthreads();
+        dma_wait<0>();     // this wave's V loads of the tile landed
+        __syncthreads();   // Q.K done everywhere (K's LDS is free); the whole V tile visible
+        if (!MASKED && more) issue_k(kt + 1);
         if (act) {
             f32x16 s;
 #pragma unroll
@@ -289,19 +301,25 @@ fwd32w_kernel(const FwdParams p) {
                 }
             }
 
+            // masked builds start the next K tile only now: their mask loads would wait on it
+            if (MASKED && more) issue_k(kt + 1);
+
             // O_g^T += V_g^T P^T : step t uses key 16*hh + t in k-slot hh
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 a = *(const f32x4*)(vl + (GD * g + 32 * db + lr) * VP + 16 * hh + 4 * q4);
+                    const f32x4 a = *(const f32x4*)(vl + (4 * hh + q4) * VQ + (GD * g + 32 * db + lr) * 4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], pv[4 * q4 + e], o[db], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();   // the next tile overwrites K, V and the partial scores
+        if (MASKED && more && !act) issue_k(kt + 1);
+        dma_wait<0>();     // this wave's K loads of the next tile landed
+        __syncthreads();   // P.V done everywhere (V and the partial scores are free), next K visible
+        if (more) issue_v(kt + 1);
     }
 
     if (!row_valid) return;

@@ -11,9 +11,9 @@ constexpr int kWaveRows = 32;
 constexpr int kThreads = 256;
 // fp32 kernel for head dims up to 128 (fa_fwd32.h): 64 rows per workgroup, four waves of 16 rows
 constexpr int kF32Rows = 64;
-// fp32 kernel for head dims 129..384 (fa_fwd32w.h): 64 rows per workgroup, six waves
+// fp32 kernel for head dims 129..384 (fa_fwd32w.h): 64 rows per workgroup, eight waves
 constexpr int kWideRows = 64;
-constexpr int kWideThreads = 384;
+constexpr int kWideThreads = 512;
 
 // Lazy rescaling threshold, in log2 units: the running row maximum is only moved when a
 // new score exceeds it by more than this, so unnormalised probabilities stay <= 2^8.
