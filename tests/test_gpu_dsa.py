@@ -41,10 +41,15 @@ CASES = {
     # no heads: every score is the bias
     "f32_no_heads": dict(seed=87, batch=1, q_seq=2, heads=0, head_dim=16, key_seq=300, top_k=10,
                          dtype="f32", bias="random"),
-    # a row longer than the selection kernel's LDS key cache (read from the workspace instead)
+    # a long row: 20 chunks of 2048 positions
     "bf16_uncached_long": dict(seed=90, batch=1, q_seq=2, heads=2, head_dim=32, key_seq=40000,
                                top_k=1000, dtype="bf16", bias="random", hole_p=0.1),
-    # many rows and a long key range
+    # every score equal (no heads, zero bias): every radix digit of every position matches the
+    # threshold's, and the winners are the lowest positions, all ties, over 5 and 2 chunks
+    "f32_all_equal_9000": dict(seed=94, batch=1, q_seq=2, heads=0, head_dim=16, key_seq=9000,
+                               top_k=3000, dtype="f32", bias="zero"),
+    "f32_all_equal_4000": dict(seed=95, batch=1, q_seq=2, heads=0, head_dim=16, key_seq=4000,
+                               top_k=1500, dtype="f32", bias="zero"),
     # ties at the threshold spread over several 2048-position chunks of a row (integer inputs:
     # a handful of distinct scores), and a multi-chunk row with fewer allowed positions than
     # top_k (-1 padding after winners from every chunk)
@@ -53,6 +58,7 @@ CASES = {
                                   scale=1.0),
     "f16_multichunk_padding": dict(seed=93, batch=1, q_seq=3, heads=4, head_dim=16, key_seq=5000,
                                    top_k=4500, dtype="f16", bias="random", hole_p=0.2),
+    # many rows and a long key range
     "bf16_rows_long": dict(seed=88, batch=2, q_seq=5, heads=16, head_dim=128, key_seq=8192,
                            top_k=2048, dtype="bf16"),
 }
