@@ -244,6 +244,10 @@ FAMILIES = {
     "fp32_d64": dict(dtype="f32", dim=64),
     "fp32_misaligned_d128": dict(dtype="f32", dim=128, misalign=True),
     "fp32_wide_d200": dict(dtype="f32", dim=200),
+    # the wide kernel's straight-line tile loads (head dim 384), and its looped ones from
+    # pointers that are 4- but not 16-byte aligned
+    "fp32_wide_d384": dict(dtype="f32", dim=384),
+    "fp32_wide_misaligned_d256": dict(dtype="f32", dim=256, misalign=True),
 }
 
 
