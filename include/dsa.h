@@ -33,7 +33,7 @@ extern "C" {
 
 /*
  * dsa_index_select -- enqueue the selection above (a scoring kernel, then the selection's
- * radix-pass, count and write kernels).
+ * histogram, candidate and write kernels).
  *
  *   query      [batch, q_seq, heads, head_dim] elements of `dtype`
  *   key        [batch, key_seq, head_dim] elements of `dtype` (one key head shared by all heads)
@@ -71,8 +71,8 @@ int dsa_check_args(const void* query, const void* key, const void* weights, cons
                    size_t workspace_bytes);
 
 /* Workspace bytes dsa_index_select needs: 4 per (batch, query row, key position) cell (the
- * cells' order keys, first), then for every query row 20496 bytes of radix histograms and
- * counters and 8 bytes per 2048 key positions; 0 when key_seq or batch * q_seq is 0, for
+ * cells' order keys, first), then for every query row 8224 bytes of histogram and counters and
+ * 4 bytes per 2048 key positions, then 8 bytes per cell (threshold candidates and positions); 0 when key_seq or batch * q_seq is 0, for
  * negative sizes or on overflow.  Host only. */
 size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq);
 

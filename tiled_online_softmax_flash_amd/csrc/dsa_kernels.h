@@ -14,16 +14,17 @@ struct DsaParams {
     const float* bias;     // [batch, 1, q_seq, key_seq]
     uint32_t* keys;        // workspace: [batch * q_seq, key_seq] order keys (0 = removed)
     int* aux;              // workspace, after the keys: [batch * q_seq, kAuxInts] per-row words
-    int* counts;           // workspace, after aux: [batch * q_seq, chunks, 2] per-chunk counts
+    int* counts;           // workspace, after aux: [batch * q_seq, chunks] per-chunk counts
+    int* cand;             // workspace, after the counts: [batch * q_seq, 2, key_seq] candidates
     int64_t* out;          // [batch, 1, q_seq, top_k]
     int64_t batch, q_seq, heads, head_dim, key_seq, top_k;
     float scale, weights_scale;
 };
 
 // Selection chunks and per-row workspace words (see dsa_select.hip): the workspace holds the
-// keys (4 bytes per cell), then kAuxInts words per row, then two words per chunk of
-// kSelChunkKeys positions of every row.
-constexpr int kAuxInts = 5124;
+// keys (4 bytes per cell), then kAuxInts words per row, then one word per chunk of
+// kSelChunkKeys positions of every row, then two words per cell (candidate keys and positions).
+constexpr int kAuxInts = 2056;
 constexpr int kSelChunkKeys = 2048;
 
 // dtype 0 f32, 1 f16, 2 bf16; head_dim <= 128.  Enqueues the scoring kernel (when key_seq > 0)

@@ -14,16 +14,20 @@
 //     float32 and read by broadcast loads.
 //   * selection, in a row's chunks of 2048 positions, one 256-thread workgroup per chunk, so
 //     that a decode step's few rows still spread over the chip.  keep = min(#allowed, top_k).
-//     The keep-th largest key is found exactly by three radix passes (digits of 11, 11 and 10
-//     bits), one kernel each:
-//     every workgroup adds its chunk's histogram of the current digit (keys that match the
-//     digits found so far) into the row's histogram in the workspace, and the next pass's
-//     workgroups each read the finished histograms back to find the digits so far.  A count
-//     kernel then gives every chunk its keys above and equal to the threshold, and a write
-//     kernel places them: every key above the threshold, and the first keys equal to it, as
-//     many as the rank left over (ties go to the lower position), in ascending position order,
-//     each chunk's slots following from the counts of the chunks before it.  The rest of the
-//     row is -1.  The scoring kernel clears the row's histograms, so a call needs no memset.
+//     The keep-th largest key (the threshold) is found exactly from its digits of 11, 11 and 10
+//     bits, in three kernels:
+//       dsa_hist_kernel: every chunk adds its histogram of the top digit into the row's (and
+//         its allowed count);
+//       dsa_cand_kernel: every chunk reads the finished histogram back, finds the threshold's
+//         top digit d0, stores its count of keys with a larger top digit, and appends its keys
+//         with top digit d0 (the candidates, with their positions) to the row's list;
+//       dsa_write_kernel: every chunk finds the threshold's other two digits among the row's
+//         candidates by itself, and from the stored counts and the candidates' positions the
+//         keys above and equal to the threshold in the chunks before it; it then places its
+//         winners: every key above the threshold, and the first keys equal to it, as many as
+//         the rank left over (ties go to the lower position), in ascending position order.
+//     The rest of the row is -1.  The scoring kernel clears the row's histogram and counters, so
+//     a call needs no memset.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
 #include <hip/hip_runtime.h>
 
@@ -168,18 +172,27 @@ __global__ void __launch_bounds__(kScoreThreads) dsa_score_kernel(const DsaParam
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), with DPP moves: within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row read 0),
+// then the last lane of row 0 added into row 1 and of row 2 into row 3 (row_bcast:15), then
+// lane 31 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, true);   // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, true);   // row_bcast:31, rows 2 and 3
+    return x;
+}
+
 // Inclusive prefix sum over the NT threads of the workgroup (thread order); `tot` gets the
 // total.  `wsum` is NT / 64 ints of LDS.  Contains barriers: every thread must call it.
 template <int NT>
 __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_inclusive_sum(v);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     int before = 0, all = 0;
@@ -193,22 +206,51 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wsum, int* tot) {
     return before + x;
 }
 
+// Two inclusive prefix sums over the NT threads with one exchange between the waves; `w2` is
+// NT / 64 pairs of ints of LDS.  Contains barriers: every thread must call it.
+template <int NT>
+__device__ __forceinline__ void block_inclusive_sum2(int a, int b, int (*w2)[2], int* pa, int* pb, int* ta, int* tb) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int xa = wave_inclusive_sum(a), xb = wave_inclusive_sum(b);
+    if (lane == 63) {
+        w2[wave][0] = xa;
+        w2[wave][1] = xb;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0, aa = 0, ab = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        if (w < wave) {
+            ba += w2[w][0];
+            bb += w2[w][1];
+        }
+        aa += w2[w][0];
+        ab += w2[w][1];
+    }
+    __syncthreads();
+    *pa = ba + xa;
+    *pb = bb + xb;
+    *ta = aa;
+    *tb = ab;
+}
+
 // ---- selection, split over chunks of a row
 constexpr int kSelThreads = 256;
 constexpr int kSelChunk = kSelChunkKeys;          // positions per workgroup: 8 per thread
 constexpr int kKeysPerThread = kSelChunk / kSelThreads;
 
-// The key is found in three radix passes over digits of 11, 11 and 10 bits (most significant
-// first).  Per-row auxiliary words after the keys in the workspace (kAuxInts per row): the three
-// passes' histograms (2048, 2048 and 1024 words), then the allowed count, the threshold key and
-// the ties to take.  Then per chunk of every row: its keys above and equal to the threshold.
-constexpr int kPasses = 3;
+// The threshold key is found by digits of 11, 11 and 10 bits (most significant first).  Per-row
+// auxiliary words after the keys in the workspace (kAuxInts per row): the histogram of the top
+// digit (2048 words), then the allowed count, the candidate count, and the row's top digit,
+// the rank left among the candidates and keep, as the candidate kernel found them.  Then per
+// chunk of every row: its keys with a larger top digit.  Then per row up to key_seq candidates
+// (keys whose top digit is the threshold's) and, after them, their positions.
 constexpr int kMaxBins = 2048;
 __host__ __device__ constexpr int pass_bits(int q) { return q < 2 ? 11 : 10; }
 __host__ __device__ constexpr int pass_shift(int q) { return q == 0 ? 21 : (q == 1 ? 10 : 0); }
-__host__ __device__ constexpr int pass_hist(int q) { return q == 0 ? 0 : (q == 1 ? 2048 : 4096); }
-constexpr int kAuxAllowed = 5120, kAuxThr = 5121, kAuxTies = 5122;
-static_assert(kAuxTies < kAuxInts, "per-row words");
+constexpr int kAuxAllowed = 2048, kAuxCand = 2049, kAuxD0 = 2050, kAuxRank = 2051, kAuxKeep = 2052;
+static_assert(kAuxKeep < kAuxInts, "per-row words");
 
 __host__ __device__ __forceinline__ int64_t sel_chunks(int64_t T) { return (T + kSelChunk - 1) / kSelChunk; }
 
@@ -249,36 +291,13 @@ __device__ __forceinline__ int find_digit(const int* hist, int nb, int rank, int
     return digit;
 }
 
-// Keys found so far: the digits of passes 0 .. npass-1 (in their bits of *prefix) and the rank
-// left among the keys that match them.  Returns keep (0: nothing is selected).
-__device__ __forceinline__ int64_t sel_state(const DsaParams& p, const int* aux, int npass, uint32_t* prefix,
-                                             int* rank, int* wsum, int* pick) {
-    const int64_t allowed = aux[kAuxAllowed];
-    const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
-    *prefix = 0u;
-    *rank = (int)keep;
-    if (keep == 0) return 0;
-    for (int q = 0; q < npass; ++q) {
-        int above;
-        const int digit = find_digit(aux + pass_hist(q), 1 << pass_bits(q), *rank, wsum, pick, &above);
-        *rank -= above;
-        *prefix |= (uint32_t)digit << pass_shift(q);
-    }
-    return keep;
-}
-
-// Radix pass PASS over one chunk: the chunk's histogram of digit PASS among the keys that match
-// the digits found so far, added into the row's histogram.  Pass 0 also counts the allowed
-// positions (keys of removed positions are 0, below every allowed key; keep <= #allowed, so they
-// never reach the threshold).
-template <int PASS>
-__global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p) {
-    constexpr int NB = 1 << pass_bits(PASS);
-    constexpr int shift = pass_shift(PASS);
-    constexpr uint32_t hi_mask = PASS == 0 ? 0u : (0xffffffffu << ((shift + pass_bits(PASS)) & 31));
+// Histogram of the top digit over one chunk, added into the row's; the allowed positions are
+// counted too (keys of removed positions are 0, below every allowed key, whose top digit is
+// never 0; keep <= #allowed, so they never reach the threshold).
+__global__ void __launch_bounds__(kSelThreads) dsa_hist_kernel(const DsaParams p) {
+    constexpr int NB = 1 << pass_bits(0);
+    constexpr int shift = pass_shift(0);
     __shared__ int hist[NB];
-    __shared__ int wsum[kSelThreads / 64];
-    __shared__ int pick[2];
     const int tid = threadIdx.x;
     const int64_t T = p.key_seq;
     const int64_t nch = sel_chunks(T);
@@ -286,16 +305,12 @@ __global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p
     const int64_t ch = (int64_t)blockIdx.x - row * nch;
     int* aux = p.aux + row * kAuxInts;
     const uint32_t* keys = p.keys + row * T;
-    // the chunk's keys are requested first, so that their latency overlaps the histogram reads
     uint32_t kk[kKeysPerThread];
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
         const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
         kk[j] = t < T ? keys[t] : 0u;
     }
-    uint32_t prefix = 0u;
-    int rank = 0;
-    if (PASS > 0 && sel_state(p, aux, PASS, &prefix, &rank, wsum, pick) == 0) return;
 #pragma unroll
     for (int i = tid; i < NB; i += kSelThreads) hist[i] = 0;
     __syncthreads();
@@ -303,26 +318,27 @@ __global__ void __launch_bounds__(kSelThreads) dsa_pass_kernel(const DsaParams p
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
         if (ch * kSelChunk + j * kSelThreads + tid < T) {
-            const uint32_t k = kk[j];
-            if (PASS == 0) allowed += k != 0u;
-            if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(NB - 1)], 1);
+            allowed += kk[j] != 0u;
+            atomicAdd(&hist[kk[j] >> shift], 1);
         }
     }
     __syncthreads();
 #pragma unroll
     for (int i = tid; i < NB; i += kSelThreads)
-        if (hist[i] != 0) atomicAdd(&aux[pass_hist(PASS) + i], hist[i]);
-    if (PASS == 0) {
-        int total;
-        block_inclusive_sum<kSelThreads>(allowed, wsum, &total);
-        if (tid == 0 && total != 0) atomicAdd(&aux[kAuxAllowed], total);
-    }
+        if (hist[i] != 0) atomicAdd(&aux[i], hist[i]);
+    // each wave adds its allowed count
+    const int wave_allowed = wave_inclusive_sum(allowed);
+    if (lane_id() == 63 && wave_allowed != 0) atomicAdd(&aux[kAuxAllowed], wave_allowed);
 }
 
-// The threshold (the keep-th largest key) and the ties to take from the three finished
-// histograms; each chunk's keys above and equal to it.
-__global__ void __launch_bounds__(kSelThreads) dsa_count_kernel(const DsaParams p) {
+// Each chunk finds, from the row's finished histogram, keep, the top digit d0 of the keep-th
+// largest key and the rank left among the keys with that digit; stores its own count of keys
+// with a larger top digit; and appends its keys with top digit d0 (the candidates) and their
+// positions to the row's list.  Chunk 0 records d0, the rank and keep.  The slots past keep are
+// set to -1 here (spread over the row's chunks).
+__global__ void __launch_bounds__(kSelThreads) dsa_cand_kernel(const DsaParams p) {
     __shared__ int wsum[kSelThreads / 64];
+    __shared__ int w2[kSelThreads / 64][2];
     __shared__ int pick[2];
     const int tid = threadIdx.x;
     const int64_t T = p.key_seq;
@@ -331,83 +347,192 @@ __global__ void __launch_bounds__(kSelThreads) dsa_count_kernel(const DsaParams 
     const int64_t ch = (int64_t)blockIdx.x - row * nch;
     int* aux = p.aux + row * kAuxInts;
     const uint32_t* keys = p.keys + row * T;
-    uint32_t kk[kKeysPerThread];   // requested before the histograms are read
-#pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j) {
-        const int64_t t = ch * kSelChunk + j * kSelThreads + tid;
-        kk[j] = t < T ? keys[t] : 0u;
-    }
-    uint32_t thr;
-    int ties;
-    if (sel_state(p, aux, kPasses, &thr, &ties, wsum, pick) == 0) return;
-    // (positions past T hold 0 here, which is below the threshold, an allowed key)
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j) {
-        gt += kk[j] > thr;
-        eq += kk[j] == thr;
-    }
-    int gt_all, eq_all;
-    block_inclusive_sum<kSelThreads>(gt, wsum, &gt_all);
-    block_inclusive_sum<kSelThreads>(eq, wsum, &eq_all);
-    if (tid == 0) {
-        p.counts[2 * (row * nch + ch)] = gt_all;
-        p.counts[2 * (row * nch + ch) + 1] = eq_all;
-        if (ch == 0) {
-            aux[kAuxThr] = (int)thr;
-            aux[kAuxTies] = ties;
-        }
-    }
-}
-
-// Output of one chunk: thread i owns positions [8 i, 8 i + 8) of the chunk.  The chunks before
-// it give the chunk's first output slot and the ties left for it; block prefix sums give each
-// thread the ties it may take (the lowest positions first) and its first slot; it writes its
-// winners in position order.  The slots past keep are -1 (spread over the row's chunks).
-__global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams p) {
-    __shared__ int wsum[kSelThreads / 64];
-    const int tid = threadIdx.x;
-    const int64_t T = p.key_seq;
-    const int64_t nch = sel_chunks(T);
-    const int64_t row = (int64_t)blockIdx.x / nch;
-    const int64_t ch = (int64_t)blockIdx.x - row * nch;
-    const int* aux = p.aux + row * kAuxInts;
-    const uint32_t* keys = p.keys + row * T;
+    int* cand_key = p.cand + row * 2 * T;
+    int* cand_pos = cand_key + T;
     int64_t* out = p.out + row * p.top_k;
-    // the chunk's keys are requested before the row's words and counts are read
     const int64_t t0 = ch * kSelChunk + (int64_t)tid * kKeysPerThread;
-    uint32_t k8[kKeysPerThread];
+    uint32_t k8[kKeysPerThread];   // requested before the histogram is read; past T: 0
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) k8[j] = t0 + j < T ? keys[t0 + j] : 0u;
     const int64_t allowed = aux[kAuxAllowed];
     const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
     for (int64_t s = keep + ch * kSelThreads + tid; s < p.top_k; s += nch * kSelThreads) out[s] = -1;
     if (keep == 0) return;
-    const uint32_t thr = (uint32_t)aux[kAuxThr];
-    const int ties_needed = aux[kAuxTies];
-    // keys above and equal to the threshold in the chunks before this one
-    int gt_b = 0, eq_b = 0;
-    for (int64_t c = tid; c < ch; c += kSelThreads) {
-        gt_b += p.counts[2 * (row * nch + c)];
-        eq_b += p.counts[2 * (row * nch + c) + 1];
+    int above;
+    const int d0 = find_digit(aux, 1 << pass_bits(0), (int)keep, wsum, pick, &above);
+    int gt_n = 0, c_n = 0;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        const int dg = (int)(k8[j] >> pass_shift(0));
+        gt_n += dg > d0;
+        c_n += dg == d0;
     }
-    int gt_before, eq_before;
-    block_inclusive_sum<kSelThreads>(gt_b, wsum, &gt_before);
-    block_inclusive_sum<kSelThreads>(eq_b, wsum, &eq_before);
-    const int ties_left = ties_needed - eq_before;   // ties this chunk and later ones may take
-    const int64_t slot0 = (int64_t)gt_before + (eq_before < ties_needed ? eq_before : ties_needed);
+    int gt_all, c_all, gt_in, c_in;
+    block_inclusive_sum2<kSelThreads>(gt_n, c_n, w2, &gt_in, &c_in, &gt_all, &c_all);
+    const int c_at = c_in - c_n;
+    if (tid == 0) {
+        p.counts[row * nch + ch] = gt_all;
+        pick[0] = c_all != 0 ? atomicAdd(&aux[kAuxCand], c_all) : 0;
+        if (ch == 0) {
+            aux[kAuxD0] = d0;
+            aux[kAuxRank] = (int)keep - above;
+            aux[kAuxKeep] = (int)keep;
+        }
+    }
+    __syncthreads();
+    int at = pick[0] + c_at;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+        if ((int)(k8[j] >> pass_shift(0)) == d0) {
+            cand_key[at] = (int)k8[j];
+            cand_pos[at] = (int)(t0 + j);
+            ++at;
+        }
+    }
+}
+
+// Digit q (1 or 2) of the rank-th largest among the row's n candidates that match `prefix` in
+// the digits above it: a histogram of this workgroup alone (LDS, zeroed and visible to every
+// thread on entry), then find_digit.  The candidate keys are read from `cand_key` (LDS or the
+// workspace).
+template <int Q, typename KeyPtr>
+__device__ __forceinline__ int cand_digit(KeyPtr cand_key, int n, uint32_t prefix, int rank, int* hist, int* wsum,
+                                          int* pick, int* above) {
+    constexpr int NB = 1 << pass_bits(Q);
+    constexpr int shift = pass_shift(Q);
+    constexpr uint32_t hi_mask = 0xffffffffu << ((shift + pass_bits(Q)) & 31);
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
+        const uint32_t k = (uint32_t)cand_key[i];
+        if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(NB - 1)], 1);
+    }
+    __syncthreads();
+    return find_digit(hist, NB, rank, wsum, pick, above);
+}
+
+// Output of one chunk: thread i owns positions [8 i, 8 i + 8) of the chunk.  The threshold (the
+// keep-th largest key) and the ties to take come from the row's candidates (the other two
+// digits, found by this workgroup alone); the chunks before this one give its first output
+// slot and the ties left for it: their stored counts of keys with a larger top digit, and their
+// candidates above and equal to the threshold.  Block prefix sums give each thread the ties it
+// may take (the lowest positions first) and its first slot; it writes its winners in position
+// order.
+constexpr int kCandLds = 2048;   // candidates the write kernel keeps in LDS (8 per thread)
+
+__global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams p) {
+    __shared__ int hist[kMaxBins];
+    __shared__ int hist2[1 << pass_bits(2)];
+    __shared__ uint32_t ck[kCandLds];
+    __shared__ int cp[kCandLds];
+    __shared__ int wsum[kSelThreads / 64];
+    __shared__ int w4[kSelThreads / 64][4];
+    __shared__ int pick[2];
+    const int tid = threadIdx.x;
+    const int64_t T = p.key_seq;
+    const int64_t nch = sel_chunks(T);
+    const int64_t row = (int64_t)blockIdx.x / nch;
+    const int64_t ch = (int64_t)blockIdx.x - row * nch;
+    const int* aux = p.aux + row * kAuxInts;
+    const int* cand_key = p.cand + row * 2 * T;
+    const int* cand_pos = cand_key + T;
+    const uint32_t* keys = p.keys + row * T;
+    int64_t* out = p.out + row * p.top_k;
+    // The chunk's keys, and the first kCandLds entries of the row's candidate list whatever the
+    // candidate count (entries past it are ignored), are requested before the row's words are
+    // read, so that the three loads share one round trip.
+    const int64_t t0 = ch * kSelChunk + (int64_t)tid * kKeysPerThread;
+    uint32_t k8[kKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) k8[j] = t0 + j < T ? keys[t0 + j] : 0u;
+    constexpr int CPT = kCandLds / kSelThreads;
+    uint32_t ckr[CPT];
+    int cpr[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int i = j * kSelThreads + tid;
+        ckr[j] = i < T ? (uint32_t)cand_key[i] : 0u;
+        cpr[j] = i < T ? cand_pos[i] : 0;
+    }
+    int gt_b = 0, eq_b = 0;   // keys above (then also equal to) the threshold before this chunk
+    for (int64_t c = tid; c < ch; c += kSelThreads) gt_b += p.counts[row * nch + c];
+    const int64_t allowed = aux[kAuxAllowed];
+    const int64_t keep = allowed < p.top_k ? allowed : p.top_k;
+    if (keep == 0) return;
+    const int n = aux[kAuxCand];
+    int rank = aux[kAuxRank];
+    uint32_t prefix = (uint32_t)aux[kAuxD0] << pass_shift(0);
+    const bool in_lds = n <= kCandLds;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        ck[j * kSelThreads + tid] = ckr[j];
+        cp[j * kSelThreads + tid] = cpr[j];
+    }
+    for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < (1 << pass_bits(2)); i += kSelThreads) hist2[i] = 0;
+    __syncthreads();
+    // the threshold's other two digits, and the candidates above and equal to it before this chunk
+    int above;
+    uint32_t thr;
+    const int64_t lim = ch * kSelChunk;
+    if (in_lds) {
+        prefix |= (uint32_t)cand_digit<1>(ck, n, prefix, rank, hist, wsum, pick, &above) << pass_shift(1);
+        rank -= above;
+        thr = prefix | (uint32_t)cand_digit<2>(ck, n, prefix, rank, hist2, wsum, pick, &above);
+        for (int i = tid; i < n; i += kSelThreads) {
+            if (cp[i] < lim) {
+                gt_b += ck[i] > thr;
+                eq_b += ck[i] == thr;
+            }
+        }
+    } else {
+        prefix |= (uint32_t)cand_digit<1>(cand_key, n, prefix, rank, hist, wsum, pick, &above) << pass_shift(1);
+        rank -= above;
+        thr = prefix | (uint32_t)cand_digit<2>(cand_key, n, prefix, rank, hist2, wsum, pick, &above);
+        for (int i = tid; i < n; i += kSelThreads) {
+            if (cand_pos[i] < lim) {
+                const uint32_t k = (uint32_t)cand_key[i];
+                gt_b += k > thr;
+                eq_b += k == thr;
+            }
+        }
+    }
+    const int ties_needed = rank - above;   // keys equal to the threshold that are taken
+    // One exchange between the waves gives the totals of gt_b and eq_b (the chunks before this
+    // one: gt_before, eq_before) and the exclusive prefixes of this chunk's own counts over the
+    // threads.  Ties go to the lowest positions: the chunk may take ties_left = ties_needed -
+    // eq_before of its own, thread i the first ones after the eq_excl ties of the threads
+    // before it, so the threads before it take min(ties_left, eq_excl) ties in all.
     int gt_n = 0, eq_n = 0;
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
         gt_n += k8[j] > thr;
         eq_n += k8[j] == thr;
     }
-    int total;
-    const int eq_in = block_inclusive_sum<kSelThreads>(eq_n, wsum, &total) - eq_n;
-    int my_ties = ties_left - eq_in;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int xg = wave_inclusive_sum(gt_n), xe = wave_inclusive_sum(eq_n);
+    const int sg = wave_inclusive_sum(gt_b), se = wave_inclusive_sum(eq_b);
+    if (lane == 63) {
+        w4[wave][0] = xg;
+        w4[wave][1] = xe;
+        w4[wave][2] = sg;
+        w4[wave][3] = se;
+    }
+    __syncthreads();
+    int gt_excl = xg - gt_n, eq_excl = xe - eq_n, gt_before = 0, eq_before = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+        if (w < wave) {
+            gt_excl += w4[w][0];
+            eq_excl += w4[w][1];
+        }
+        gt_before += w4[w][2];
+        eq_before += w4[w][3];
+    }
+    const int ties_left = ties_needed - eq_before > 0 ? ties_needed - eq_before : 0;
+    const int64_t slot0 = (int64_t)gt_before + (eq_before < ties_needed ? eq_before : ties_needed);
+    int my_ties = ties_left - eq_excl;
     my_ties = my_ties < 0 ? 0 : (my_ties > eq_n ? eq_n : my_ties);
-    const int sel = gt_n + my_ties;
-    int64_t slot = slot0 + block_inclusive_sum<kSelThreads>(sel, wsum, &total) - sel;
+    int64_t slot = slot0 + gt_excl + (ties_left < eq_excl ? ties_left : eq_excl);
     int ties_taken = 0;
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
@@ -453,11 +578,8 @@ hipError_t launch_index_select(const DsaParams& p, int dtype, hipStream_t s) {
                               : (dtype == 1 ? launch_score<_Float16>(p, s) : launch_score<uint16_t>(p, s));
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(rows * sel_chunks(p.key_seq)));
-    static_assert(kPasses == 3, "one launch per pass");
-    hipLaunchKernelGGL(dsa_pass_kernel<0>, grid, dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL(dsa_pass_kernel<1>, grid, dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL(dsa_pass_kernel<2>, grid, dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL(dsa_count_kernel, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_hist_kernel, grid, dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(dsa_cand_kernel, grid, dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(dsa_write_kernel, grid, dim3(kSelThreads), 0, s, p);
     return hipGetLastError();
 }

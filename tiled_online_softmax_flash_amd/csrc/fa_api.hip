@@ -390,12 +390,14 @@ size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq) {
     int64_t keys, rows;
     if (!count4(batch, q_seq, key_seq, 4, &keys) || !count4(batch, q_seq, 1, 1, &rows)) return 0;
     if (key_seq == 0 || rows == 0) return 0;
-    // keys, then per row kAuxInts words and two words per chunk of kSelChunkKeys positions
+    // keys, then per row kAuxInts words and one word per chunk of kSelChunkKeys positions, then
+    // two words per cell (the candidates)
     const int64_t chunks = ((int64_t)key_seq + dsa::kSelChunkKeys - 1) / dsa::kSelChunkKeys;
     int64_t aux, cnt, total;
-    if (!mul_ok(rows, (int64_t)dsa::kAuxInts * 4, &aux) || !mul_ok(rows, chunks * 8, &cnt)) return 0;
+    if (!mul_ok(rows, (int64_t)dsa::kAuxInts * 4, &aux) || !mul_ok(rows, chunks * 4, &cnt)) return 0;
     total = keys + aux + cnt;
-    if (total < keys) return 0;
+    if (total < keys || total > INT64_MAX - 2 * keys) return 0;
+    total += 2 * keys;
     return (size_t)total;
 }
 
@@ -461,6 +463,7 @@ int dsa_index_select(const void* query, const void* key, const void* weights, co
     p.keys = (uint32_t*)workspace;
     p.aux = (int*)((char*)workspace + (size_t)batch * q_seq * key_seq * 4);
     p.counts = p.aux + (size_t)batch * q_seq * dsa::kAuxInts;
+    p.cand = p.counts + (size_t)batch * q_seq * (((size_t)key_seq + dsa::kSelChunkKeys - 1) / dsa::kSelChunkKeys);
     p.out = out;
     p.batch = batch;
     p.q_seq = q_seq;
