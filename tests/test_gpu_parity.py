@@ -146,6 +146,10 @@ EDGE = {
                                    softcap=3.0),
     "fp32_d129_token_major": dict(seed=53, batch=2, heads=3, kv_heads=3, sq=65, sk=65, dim=129,
                                   dtype="f32", out_layout="token"),
+    # 256 tiles of 64 rows: on 256 CUs the fp32 kernel keeps whole 64-row workgroups here (the
+    # key-split form takes the other fp32 cases: too few tiles, or a fractional number per CU)
+    "fp32_d128_whole_tiles": dict(seed=94, batch=1, heads=8, kv_heads=8, sq=2048, sk=150, dim=128,
+                                  dtype="f32", causal=True),
     # wide fp32 head dims on whole 64-dim runs below 384 (the K dims past them are never loaded)
     # and a 16-dim-aligned one, with an additive mask and no softcap
     "fp32_d256_mask": dict(seed=91, batch=1, heads=3, kv_heads=1, sq=90, sk=150, dim=256,

@@ -53,6 +53,9 @@ struct Plan {
     bool ring;  // 256-row LDS-ring kernel (16-bit, head dim 64/128, aligned rows)
     bool wide;  // fp32 kernel for head dims 129..384
     bool empty;
+    // fp32 (head dim <= 128) in 32-row workgroups with the key range split in two halves: grid
+    // and tile counts (grid_split 0 where that form is not available)
+    int grid_split, q_tiles_split, pairs_split;
 };
 
 int validate(const void* q, const void* k, const void* v, const void* mask, const void* out,
@@ -131,6 +134,18 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     if (!mul_ok(xcd_groups ? (int64_t)batch * q_tiles : pairs_padded, heads, &grid) || grid > 0x7fffffffLL)
         return fail(FA_ERR_OVERFLOW, "grid of %lld x %d workgroups exceeds the launch limit",
                     (long long)pairs_padded, heads);
+
+    plan->grid_split = 0;
+    if (dtype == FA_DTYPE_F32 && !plan->wide) {
+        const int64_t qt2 = ((int64_t)sq + fa::kF32SplitRows - 1) / fa::kF32SplitRows;
+        const int64_t pairs2 = (int64_t)batch * qt2;
+        int64_t grid2;
+        if (mul_ok(xcd_groups ? pairs2 : (pairs2 + 7) / 8 * 8, heads, &grid2) && grid2 <= 0x7fffffffLL) {
+            plan->grid_split = (int)grid2;
+            plan->q_tiles_split = (int)qt2;
+            plan->pairs_split = (int)pairs2;
+        }
+    }
 
     fa::FwdParams& p = plan->p;
     p.q = q; p.k = k; p.v = v; p.out = (void*)out;
@@ -329,6 +344,25 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
         const int persist = cus / 8 * 8;
         if (persist >= 8 && grid > persist) grid = persist;
     }
+    // fp32: the key-split form when its twice as many half-size workgroups spread more evenly
+    // over the CUs.  Per CU, in units of one 64-row workgroup's work: ceil(n / cus) whole ones
+    // against ceil(2n / cus) halves, a half costing about 0.58 of a whole one (its K/V tiles
+    // serve 32 rows instead of 64: measured on the fp32 DiT problem, 24 heads x 1536 rows, where
+    // 2.25 whole workgroups per CU take 297 us and 4.5 halves 290 us).
+    bool split = false;
+    if (dtype == FA_DTYPE_F32 && !plan.wide && plan.grid_split > 0 &&
+        fa::fwd32_split_built(plan.dp, plan.maskk != 0)) {
+        const int cus = device_cu_count();
+        if (cus <= 0) return fail(FA_ERR_HIP, "cannot query the compute-unit count of the current device");
+        const int64_t whole = ((int64_t)plan.grid + cus - 1) / cus;
+        const int64_t halves = ((int64_t)plan.grid_split + cus - 1) / cus;
+        if (7 * halves < 12 * whole) {
+            split = true;
+            grid = plan.grid_split;
+            p.q_tiles = plan.q_tiles_split;
+            p.pairs = plan.pairs_split;
+        }
+    }
     hipError_t err;
     if (dtype == FA_DTYPE_BF16)
         err = plan.ring ? fa::launch_bf16_ring(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s)
@@ -337,7 +371,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, const void* mask
         err = plan.ring ? fa::launch_f16_ring(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s)
                         : fa::launch_f16(p, plan.dp, grid, plan.maskk, p.softcap > 0.0f, s);
     else if (plan.wide) err = fa::launch_f32_wide(p, grid, plan.maskk != 0, p.softcap > 0.0f, s);
-    else err = fa::launch_f32(p, plan.dp, grid, plan.maskk != 0, p.softcap > 0.0f, s);
+    else err = fa::launch_f32(p, plan.dp, grid, plan.maskk != 0, p.softcap > 0.0f, split, s);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return FA_OK;
 }

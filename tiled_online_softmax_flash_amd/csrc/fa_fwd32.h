@@ -45,7 +45,12 @@ __device__ __forceinline__ float row4_sum(float x) {
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 
 // RAW: no mask, no softcap and scale > 0 (scale folded into the base-2 exponent factor).
-template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
+// SPLIT: a workgroup takes 32 rows (two 16-row groups) and its key range in two halves: wave w
+// covers row group w % 2 over key half w / 2, each half with its own (single) K/V tile buffer in
+// LDS, and the two waves of a row group merge their results at the end.  A problem of n 64-row
+// tiles then makes 2n half-size workgroups, which spread evenly over the CUs where n does not
+// (n = 2.25 per CU leaves a quarter of the CUs a third workgroup; 4.5 half-size ones do not).
+template <int DP, bool MASKED, bool SOFTCAP, bool RAW, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3)))
 fwd32_kernel(const FwdParams p) {
     constexpr int BN = 16;              // keys per tile
@@ -59,9 +64,11 @@ fwd32_kernel(const FwdParams p) {
     constexpr int NDB = DP / 16;        // 16-dim output blocks
     constexpr int CPR = DP / 4;         // 16-byte chunks per K/V row
     constexpr int NCH = BN * CPR;       // chunks per K (or V) tile
-    constexpr int NLD = (NCH + kThreads - 1) / kThreads;
+    constexpr int NTH = SPLIT ? kThreads / 2 : kThreads;   // threads that load one tile
+    constexpr int NLD = (NCH + NTH - 1) / NTH;
+    constexpr int ROWS = SPLIT ? kF32SplitRows : kF32Rows;  // query rows per workgroup
     static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
-    static_assert(kF32Rows == 4 * WR && kThreads == 256, "four 16-row waves");
+    static_assert(kF32Rows == 4 * WR && kF32SplitRows == 2 * WR && kThreads == 256, "four 16-row waves");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * (KSZ + VSZ)];
 
@@ -71,6 +78,9 @@ fwd32_kernel(const FwdParams p) {
     const int kvh = h / p.group;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+    const int rg = SPLIT ? (wave & 1) : wave;                    // the wave's row group
+    const int kh = SPLIT ? (wave >> 1) : 0;                      // SPLIT: the wave's key half
+    const int th = SPLIT ? tid - kh * NTH : tid;                 // thread among its tile's loaders
     const int lane = tid & 63;
     const int r = lane & 15;
     const int s = lane >> 4;
@@ -78,9 +88,9 @@ fwd32_kernel(const FwdParams p) {
 
     const KeyRule rule = make_rule(p, b);
     const int Lk = (int)rule.L;         // keys < sk <= INT32_MAX
-    const int64_t q0 = (int64_t)w.qt * kF32Rows;
-    const int64_t q_last = (q0 + kF32Rows < p.sq ? q0 + kF32Rows : p.sq) - 1;
-    const int64_t wr0 = q0 + wave * WR;
+    const int64_t q0 = (int64_t)w.qt * ROWS;
+    const int64_t q_last = (q0 + ROWS < p.sq ? q0 + ROWS : p.sq) - 1;
+    const int64_t wr0 = q0 + rg * WR;
     const bool wave_has_rows = wr0 < p.sq;
     const int64_t wr1 = (wr0 + WR - 1 < p.sq ? wr0 + WR - 1 : p.sq - 1);
     const int64_t row = wr0 + r;
@@ -164,8 +174,8 @@ fwd32_kernel(const FwdParams p) {
     int k_lds[NLD], v_lds[NLD];
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-        const int u = tid + kThreads * n;
-        const bool in = NCH % kThreads == 0 || u < NCH;
+        const int u = th + NTH * n;
+        const bool in = NCH % NTH == 0 || u < NCH;
         const int kr = u / CPR, kc = (u % CPR) * 4;
         const int vr = u % BN, vc = (u / BN) * 4;
         k_cnt[n] = in ? (D - kc < 0 ? 0 : (D - kc > 4 ? 4 : D - kc)) : 0;
@@ -204,12 +214,11 @@ fwd32_kernel(const FwdParams p) {
         }
     };
 
-    auto store_tile = [&](auto buf_tag) {
-        float* kl = lds + decltype(buf_tag)::value * (KSZ + VSZ);
+    auto store_tile = [&](float* kl) {
         float* vl = kl + KSZ;
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            if (NCH % kThreads != 0 && tid + kThreads * n >= NCH) continue;
+            if (NCH % NTH != 0 && th + NTH * n >= NCH) continue;
             *(f32x4*)(kl + k_lds[n]) = kreg[n];
 #pragma unroll
             for (int e = 0; e < 4; ++e) vl[v_lds[n] + e * VP] = vreg[n][e];
@@ -230,8 +239,7 @@ fwd32_kernel(const FwdParams p) {
         return val;
     };
 
-    auto compute_tile = [&](auto buf_tag, int kt, const f32x4& mval) {
-        const float* kl = lds + decltype(buf_tag)::value * (KSZ + VSZ);
+    auto compute_tile = [&](const float* kl, int kt, const f32x4& mval) {
         const float* vl = kl + KSZ;
 
         // S^T = K Q^T, in two interleaved chains (even and odd steps) so that consecutive
@@ -326,7 +334,7 @@ fwd32_kernel(const FwdParams p) {
         f32x4 mcur = f32x4(0.0f);
         if (MASKED && wave_needs(kt_begin)) mcur = load_mask(kt_begin);
         load_tile(vec_tag, kt_begin);
-        store_tile(std::integral_constant<int, 0>{});
+        store_tile(lds);
         __syncthreads();
         // tile t sits in buffer t % 2; two tiles per trip so that the buffer is a constant
         auto step = [&](auto buf_tag, int t) {
@@ -338,8 +346,8 @@ fwd32_kernel(const FwdParams p) {
                 load_tile(vec_tag, kt + 1);
                 if (MASKED && wave_needs(kt + 1)) mnext = load_mask(kt + 1);
             }
-            if (wave_needs(kt)) compute_tile(buf_tag, kt, mcur);
-            if (more) store_tile(std::integral_constant<int, BUF ^ 1>{});
+            if (wave_needs(kt)) compute_tile(lds + BUF * (KSZ + VSZ), kt, mcur);
+            if (more) store_tile(lds + (BUF ^ 1) * (KSZ + VSZ));
             __syncthreads();
             mcur = mnext;
         };
@@ -348,9 +356,74 @@ fwd32_kernel(const FwdParams p) {
             if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
         }
     };
+    // SPLIT: key half kh takes tiles [kt_begin + kh n0, ...): n0 = ceil(n_tiles / 2) of them for
+    // half 0, the rest for half 1, each through its own buffer (the next tile is loaded into
+    // registers under this one's products, stored after a barrier).  Both halves run n0 trips
+    // so that every wave reaches every barrier.
+    const int n0 = (n_tiles + 1) / 2;
+    auto split_loop = [&](auto vec_tag) {
+        const int first = kt_begin + kh * n0;
+        const int mine = kh ? n_tiles - n0 : n0;
+        float* const buf = lds + kh * (KSZ + VSZ);
+        f32x4 mcur = f32x4(0.0f);
+        if (mine > 0) {
+            if (MASKED && wave_needs(first)) mcur = load_mask(first);
+            load_tile(vec_tag, first);
+            store_tile(buf);
+        }
+        __syncthreads();
+        for (int t = 0; t < n0; ++t) {
+            const int kt = first + t;
+            const bool more = t + 1 < mine;
+            f32x4 mnext = f32x4(0.0f);
+            if (more) {
+                load_tile(vec_tag, kt + 1);
+                if (MASKED && wave_needs(kt + 1)) mnext = load_mask(kt + 1);
+            }
+            if (t < mine && wave_needs(kt)) compute_tile(buf, kt, mcur);
+            __syncthreads();   // the tile's products are done in both halves
+            if (more) store_tile(buf);
+            __syncthreads();   // the next tile visible
+            mcur = mnext;
+        }
+    };
     if (n_tiles > 0) {
-        if (p.vec_kv) main_loop(std::true_type{});
-        else main_loop(std::false_type{});
+        if constexpr (SPLIT) {
+            if (p.vec_kv) split_loop(std::true_type{});
+            else split_loop(std::false_type{});
+        } else {
+            if (p.vec_kv) main_loop(std::true_type{});
+            else main_loop(std::false_type{});
+        }
+    }
+
+    if constexpr (SPLIT) {
+        // the key-half-1 wave of each row group hands its running maximum, sum share and O to
+        // the key-half-0 wave (lane by lane: both hold the same rows and k-slots), which merges
+        // them: both parts are rescaled to the larger maximum (a part with no maximum yet adds 0)
+        constexpr int MW = 2 + 4 * NDB;      // words per lane
+        static_assert(2 * 64 * MW <= 2 * (KSZ + VSZ), "merge area inside the tile buffers");
+        float* const mb = lds + rg * 64 * MW + lane;
+        __syncthreads();   // (n_tiles == 0: no loop barrier) the tile buffers are free
+        if (kh == 1) {
+            mb[0] = m_run;
+            mb[64] = l_run;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mb[64 * (2 + 4 * db + i)] = o[db][i];
+        }
+        __syncthreads();
+        if (kh == 1) return;   // no barrier follows
+        const float m1 = mb[0];
+        const float mm = __builtin_fmaxf(m_run, m1);
+        const float a0 = m_run == neg_inf() ? 0.0f : exp2_hw((m_run - mm) * kfac);
+        const float a1 = m1 == neg_inf() ? 0.0f : exp2_hw((m1 - mm) * kfac);
+        l_run = l_run * a0 + mb[64] * a1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a0 + mb[64 * (2 + 4 * db + i)] * a1;
     }
 
     // every lane takes part in the row sums before the invalid rows leave
@@ -374,27 +447,38 @@ fwd32_kernel(const FwdParams p) {
 }
 
 template <int DP, bool MASKED, bool SOFTCAP, bool RAW>
-hipError_t launch_fwd32_one(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd32_kernel<DP, MASKED, SOFTCAP, RAW>), dim3(grid), dim3(kThreads), 0, stream, p);
+hipError_t launch_fwd32_one(const FwdParams& p, int grid, bool split, hipStream_t stream) {
+    if constexpr (fwd32_split_built(DP, MASKED)) {
+        if (split) {
+            hipLaunchKernelGGL((fwd32_kernel<DP, MASKED, SOFTCAP, RAW, true>), dim3(grid), dim3(kThreads), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+    } else {
+        if (split) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((fwd32_kernel<DP, MASKED, SOFTCAP, RAW, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DP>
-hipError_t launch_fwd32_dp(const FwdParams& p, int grid, bool masked, bool softcap, hipStream_t s) {
-    if (softcap) return masked ? launch_fwd32_one<DP, true, true, false>(p, grid, s)
-                               : launch_fwd32_one<DP, false, true, false>(p, grid, s);
-    if (masked) return launch_fwd32_one<DP, true, false, false>(p, grid, s);
-    return p.raw_scores ? launch_fwd32_one<DP, false, false, true>(p, grid, s)
-                        : launch_fwd32_one<DP, false, false, false>(p, grid, s);
+hipError_t launch_fwd32_dp(const FwdParams& p, int grid, bool masked, bool softcap, bool split, hipStream_t s) {
+    if (softcap) return masked ? launch_fwd32_one<DP, true, true, false>(p, grid, split, s)
+                               : launch_fwd32_one<DP, false, true, false>(p, grid, split, s);
+    if (masked) return launch_fwd32_one<DP, true, false, false>(p, grid, split, s);
+    return p.raw_scores ? launch_fwd32_one<DP, false, false, true>(p, grid, split, s)
+                        : launch_fwd32_one<DP, false, false, false>(p, grid, split, s);
 }
 
 // Head dims 65..96 take the 128-dim build (dims past D are zero): a 96-dim build needs more
-// registers than three waves per SIMD allow.
-inline hipError_t launch_fwd32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, hipStream_t s) {
+// registers than three waves per SIMD allow.  split: 32-row workgroups with the key range in two
+// halves (the grid and p.q_tiles counted in 32-row tiles).
+inline hipError_t launch_fwd32(const FwdParams& p, int dp, int grid, bool masked, bool softcap, bool split,
+                               hipStream_t s) {
     switch (dp) {
-        case 32: return launch_fwd32_dp<32>(p, grid, masked, softcap, s);
-        case 64: return launch_fwd32_dp<64>(p, grid, masked, softcap, s);
-        default: return launch_fwd32_dp<128>(p, grid, masked, softcap, s);
+        case 32: return launch_fwd32_dp<32>(p, grid, masked, softcap, split, s);
+        case 64: return launch_fwd32_dp<64>(p, grid, masked, softcap, split, s);
+        default: return launch_fwd32_dp<128>(p, grid, masked, softcap, split, s);
     }
 }
 

@@ -11,6 +11,10 @@ constexpr int kWaveRows = 32;
 constexpr int kThreads = 256;
 // fp32 kernel for head dims up to 128 (fa_fwd32.h): 64 rows per workgroup, four waves of 16 rows
 constexpr int kF32Rows = 64;
+constexpr int kF32SplitRows = 32;   // fp32 workgroups whose key range is split in two halves
+// The key-split form is not built for masked head-dim-128 problems (it would spill registers at
+// three waves per SIMD).
+constexpr bool fwd32_split_built(int dp, bool masked) { return !(masked && dp > 64); }
 // fp32 kernel for head dims 129..384 (fa_fwd32w.h): 64 rows per workgroup, eight waves
 constexpr int kWideRows = 64;
 constexpr int kWideThreads = 512;
