@@ -135,7 +135,7 @@ EDGE = {
     # loaded during the current one's last steps; ragged last query tile
     "many_items_per_workgroup": dict(seed=47, batch=8, heads=32, kv_heads=8, sq=520, sk=520,
                                      dim=128, dtype="bf16", causal=True),
-    # fp32 head dims 129..384 (three 128-dim groups; dims past D in the last group unused)
+    # fp32 head dims 129..384 (four 96-dim groups; dims past D in the last groups unused)
     "fp32_d384_gqa_causal_lengths": dict(seed=50, batch=2, heads=4, kv_heads=2, sq=150, sk=170,
                                          dim=384, dtype="f32", causal=True, lengths="past",
                                          max_past=20),
