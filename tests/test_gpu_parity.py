@@ -146,6 +146,15 @@ EDGE = {
                                    softcap=3.0),
     "fp32_d129_token_major": dict(seed=53, batch=2, heads=3, kv_heads=3, sq=65, sk=65, dim=129,
                                   dtype="f32", out_layout="token"),
+    # the fp32 key-split form (small problems take it): one key tile, so the second key half
+    # has nothing to do; causal rows whose keys all fall in the first half; a window narrower
+    # than a tile, where each half holds keys for some row groups only; a ragged 32-row tile
+    "fp32_split_one_key_tile": dict(seed=95, batch=1, heads=2, kv_heads=1, sq=45, sk=10, dim=64,
+                                    dtype="f32"),
+    "fp32_split_causal_odd_tiles": dict(seed=96, batch=2, heads=2, kv_heads=2, sq=83, sk=83,
+                                        dim=128, dtype="f32", causal=True),
+    "fp32_split_narrow_window": dict(seed=97, batch=1, heads=3, kv_heads=1, sq=100, sk=140,
+                                     dim=32, dtype="f32", causal=True, local_window=9),
     # 256 tiles of 64 rows: on 256 CUs the fp32 kernel keeps whole 64-row workgroups here (the
     # key-split form takes the other fp32 cases: too few tiles, or a fractional number per CU)
     "fp32_d128_whole_tiles": dict(seed=94, batch=1, heads=8, kv_heads=8, sq=2048, sk=150, dim=128,
