@@ -184,6 +184,13 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     else p.kfac = 1.4426950408889634f;                                        // x in natural units
     if (!std::isfinite(p.kfac) || !(p.kfac > 0.0f))
         return fail(FA_ERR_UNSUPPORTED, "softcap %g is too large for fp32 exponent scaling", (double)softcap);
+    // Masked bf16 head-dim-64 ring launches whose scale is a power of two in [2^-20, 1] (the
+    // default 1/8 included): the kernel multiplies Q by the scale, which only moves bf16 exponents
+    // (exact above 2^-123 in magnitude), and starts the Q.K products from the mask values.
+    int scale_exp = 0;
+    const float scale_mant = std::frexp(scale, &scale_exp);
+    p.mask_in_acc = (plan->ring && dtype == FA_DTYPE_BF16 && mask_planes > 0 && !has_cap && dim == 64 &&
+                     scale_mant == 0.5f && scale_exp >= -19 && scale_exp <= 1) ? 1 : 0;
     plan->dp = plan->wide ? 384 : (dim + 31) / 32 * 32;
     plan->grid = (int)grid;
     return FA_OK;

@@ -113,6 +113,12 @@ fwd16_ring_kernel(const FwdParams p) {
     // lookups, not the bytes, bounded the kernel.
     constexpr bool MASK_AHEAD = MASKED && DP == 64;
     constexpr bool MASK_LDS = MASK_AHEAD && MASKK == kMaskF32 && RB == 1;
+    // RAW with a mask: the scale is a power of two that Q takes exactly (multiplied in once per
+    // item), and each half-tile's Q.K products start from its mask values instead of zero, so
+    // the accumulators hold scale * (Q.K) + mask and the scores need no per-element
+    // multiply-add.  Needs the mask a block before its softmax: the head-dim-64 schedule.
+    constexpr bool MASK_ACC = MASKED && RAW;
+    static_assert(!MASK_ACC || (MASK_AHEAD && SOFTCAP == 0), "mask accumulation needs the mask-ahead schedule");
     constexpr int MSK_WAVE = 2 * 32 * 128;   // one step's fp32 mask of a wave: 2 half-tiles x 32 rows x 128 B
     // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
     // a step's mask values as well, and the head-dim-128 variants with a softcap or a scale
@@ -370,6 +376,11 @@ fwd16_ring_kernel(const FwdParams p) {
                 u32x4 t = __builtin_bit_cast(u32x4, qf[rb][ks]);
                 asm volatile("" : "+v"(t));
                 qf[rb][ks] = row_valid[rb] ? __builtin_bit_cast(vec8, t) : vec8((scalar)0.0f);
+                if constexpr (MASK_ACC) {
+                    // exact: a power-of-two scale only moves the exponent
+                    typedef float f32x8 __attribute__((ext_vector_type(8)));
+                    qf[rb][ks] = __builtin_convertvector(__builtin_convertvector(qf[rb][ks], f32x8) * p.scale, vec8);
+                }
             }
         }
     };
@@ -377,13 +388,16 @@ fwd16_ring_kernel(const FwdParams p) {
     // ---- mask rows of this workgroup (rows are 16-byte aligned: the dispatcher checks it)
     constexpr uint32_t MESZ = MASKK == kMaskF32 ? 4u : 2u;
     u32x4 rmask = u32x4{0u, 0u, 0u, 0u};
+    const char* mbase = nullptr;   // the item's first mask row
+    int64_t mask_bytes = 0;        // bytes of the item's mask rows
     uint32_t mask_row_off[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mask_row_off[rb] = 0;
     if constexpr (MASKED) {
         const int64_t rows_here = q_last - q0 + 1;
-        const char* mbase = (const char*)p.mask + ((mask_plane(p, b, h) * p.sq + q0) * (int64_t)p.sk) * MESZ;
-        rmask = make_rsrc_words(mbase, (int)(rows_here * p.sk * MESZ));
+        mbase = (const char*)p.mask + ((mask_plane(p, b, h) * p.sq + q0) * (int64_t)p.sk) * MESZ;
+        mask_bytes = rows_here * p.sk * MESZ;
+        rmask = make_rsrc_words(mbase, (int)mask_bytes);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mask_row_off[rb] = (uint32_t)((row[rb] - q0) * (int64_t)p.sk) * MESZ;
     }
@@ -456,8 +470,13 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (MASK_LDS) {
             constexpr int j = decltype(j_c)::value;
             const uint32_t dst = lds_base + (uint32_t)(MSK_OFF + wave * MSK_WAVE);
-            const uint32_t koff = (uint32_t)half_k0(2 * s + 1 + j / 4) * 4u + (uint32_t)(j % 4) * msk_row8;
-            dma_lds16(rmask, dst + 1024u * j, msk_src + koff);
+            // The descriptor starts at the half-tile's first key of the item's first row (and ends
+            // where the item's mask rows end), so that the lane offsets stay fixed: the same
+            // bounds check as an offset from the rows' start, with no per-load vector addition.
+            const int64_t koff = (int64_t)half_k0(2 * s + 1 + j / 4) * 4;
+            const int64_t left = mask_bytes - koff;
+            const u32x4 rm = make_rsrc_words(mbase + koff, left > 0 ? (int)left : 0);
+            dma_lds16(rm, dst + 1024u * j, msk_src + (uint32_t)(j % 4) * msk_row8);
         }
     };
     auto mask_dma = [&](int s) __attribute__((always_inline)) {
@@ -526,6 +545,8 @@ fwd16_ring_kernel(const FwdParams p) {
         if constexpr (SOFTCAP) {
             const float th = tanh_fast(sv * p.cap_y);
             return MASKED ? __builtin_fmaf(p.softcap, th, mvv) : th;
+        } else if constexpr (MASK_ACC) {
+            return sv;   // scale * (Q.K) + mask, formed by the products
         } else if constexpr (MASKED) {
             return __builtin_fmaf(sv, p.scale, mvv);
         } else if constexpr (!RAW) {
@@ -755,7 +776,8 @@ fwd16_ring_kernel(const FwdParams p) {
     // would score half-tiles past the item.  kBlkEnd: no block follows in this item.
     auto xbody = [&](auto full_c, auto mode_c, auto par_c, uint32_t v_slot, uint32_t k_slot, int u,
                      f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], u32x4 (&p_prev)[RB][2], u32x4 (&p_cur)[RB][2],
-                     const MaskH (&mh)[RB], u32x2 (&rpre)[NPRE], auto&& unit_hook) __attribute__((always_inline)) {
+                     const MaskH (&mh)[RB], const MaskH (&mq)[RB], u32x2 (&rpre)[NPRE], auto&& unit_hook)
+                     __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_c)::value;
         constexpr bool WITH_PV = (MODE & kBlkPV) != 0;
         constexpr bool WITH_QK = (MODE & kBlkQK) != 0;
@@ -841,7 +863,13 @@ fwd16_ring_kernel(const FwdParams p) {
                 o[rb][db] = Tr::mfma(__builtin_bit_cast(vec8, frag), __builtin_bit_cast(vec8, p_prev[rb][j]), o[rb][db]);
             } else {
                 constexpr int ks = f - NPV;
-                s_nxt[rb] = Tr::mfma(__builtin_bit_cast(vec8, frag), qf[rb][ks], ks == 0 ? f32x16(0.0f) : s_nxt[rb]);
+                f32x16 c0 = f32x16(0.0f);
+                if constexpr (MASK_ACC) {
+                    // the mask of half-tile u+1, element v at accumulator element v
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) c0[v] = mask_val(mq[rb], v);
+                }
+                s_nxt[rb] = Tr::mfma(__builtin_bit_cast(vec8, frag), qf[rb][ks], ks == 0 ? c0 : s_nxt[rb]);
             }
             // softmax phases of the RB row blocks, interleaved (slot q: phase q / RB of row block q % RB)
             if constexpr (WITH_SM) {
@@ -923,7 +951,10 @@ fwd16_ring_kernel(const FwdParams p) {
             // the buffer holds this step's successor's mask (DMA of two steps back): read it out,
             // then refill the buffer with the mask of the step after that
             // (its refill is spread over the first block below, or issued here in a skip step)
-            mask_from_lds(mnext);
+            // (steps after the first read it out at the end of the step before, ahead of that
+            // step's barrier, so that the read's latency overlaps the barrier's wait; the wait
+            // here keeps the refill from overwriting the buffer before the reads are done)
+            if constexpr (PHASE == 0) mask_from_lds(mnext);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if constexpr (KIND == 0) mask_dma(t + 2);
         } else if constexpr (MASK_AHEAD) {
@@ -990,10 +1021,13 @@ fwd16_ring_kernel(const FwdParams p) {
             // every step alone.  Raising the younger wave's priority for the first block lets
             // the pair finish a step together more closely.
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(1);
-            xbody(F{}, int_c<MODE_A>{}, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0], rpre, hook_a);
+            // (block 2t+1 scores half-tile 2t+2, whose mask is mcur[1]; block 2t+2 scores half-tile
+            // 2t+3, whose mask mnext[0] was read out at the start of this step)
+            xbody(F{}, int_c<MODE_A>{}, int_c<0>{}, v_slot, k_slot, 2 * t + 1, s_odd, s_even, p_even, p_odd, mcur[0],
+                  mcur[1], rpre, hook_a);
             if (wave >= WAVES / 2) __builtin_amdgcn_s_setprio(0);
-            xbody(F{}, int_c<MODE_B>{}, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1], rpre,
-                  hook_b);
+            xbody(F{}, int_c<MODE_B>{}, int_c<1>{}, v_slot, k_slot, 2 * t + 2, s_even, s_odd, p_odd, p_even, mcur[1],
+                  mnext[0], rpre, hook_b);
         }
         if constexpr (!EARLY) {
             ring_wait();   // everything but tile t+3 landed
@@ -1001,6 +1035,9 @@ fwd16_ring_kernel(const FwdParams p) {
                 launder_mask(mnext[0]);
                 launder_mask(mnext[1]);
             }
+            // MASK_LDS: the buffer now holds the mask of step t+2 (this step's refill landed),
+            // which the next step holds as its mnext, this step's mcur (no longer read)
+            if constexpr (MASK_LDS) mask_from_lds(mcur);
             __syncthreads();
         }
     };
@@ -1156,6 +1193,13 @@ hipError_t launch_ring_dp(const FwdParams& p, int grid, int maskk, bool softcap,
                             : launch_ring_one<Tr, DP, kMaskT, 1, false>(p, grid, s);
         return identity ? launch_ring_one<Tr, DP, kMaskNone, 2, false>(p, grid, s)
                         : launch_ring_one<Tr, DP, kMaskNone, 1, false>(p, grid, s);
+    }
+    // (mask accumulation: bf16 only, whose exponent range lets Q take the scale exactly)
+    if constexpr (DP == 64 && std::is_same<Tr, TraitsBF16>::value) {
+        if (p.mask_in_acc) {
+            if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, true>(p, grid, s);
+            if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, true>(p, grid, s);
+        }
     }
     if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, false>(p, grid, s);
     if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, false>(p, grid, s);

@@ -48,6 +48,8 @@ struct FwdParams {
     int vec_mask;                // mask rows move in 16-byte pieces
     int vec_out;                 // output rows move in 4-element pieces
     int raw_scores;              // 1: scores stay raw dot products, scale folded into kfac
+    int mask_in_acc;             // 1: Q is pre-multiplied by the (power-of-two) scale and the
+                                 //    ring kernel's Q.K products start from the mask values
     float scale;
     float softcap;
     float cap_y;                 // scale / softcap: dot product -> tanh argument
