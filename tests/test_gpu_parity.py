@@ -200,6 +200,13 @@ EDGE = {
     "mask_acc_scale_2m5_bf16mask": dict(seed=65, batch=2, heads=2, kv_heads=1, sq=150, sk=260,
                                         dim=64, dtype="bf16", scale=2.0 ** -5, mask="ramp",
                                         mask_ramp=0.25, mask_p=0.1, mask_dtype="bf16", causal=True),
+    # softcaps at which many scores straddle |s / c| = 1/8, where the speculative softmax's
+    # polynomial form of c tanh(s / c) ends and rows are redone with the exact form
+    "softcap_series_edge_f16_d128": dict(seed=67, batch=2, heads=4, kv_heads=2, sq=300, sk=400,
+                                         dim=128, dtype="f16", softcap=8.0, causal=True),
+    "softcap_series_edge_bf16_d64": dict(seed=68, batch=2, heads=4, kv_heads=1, sq=280, sk=520,
+                                         dim=64, dtype="bf16", softcap=4.0, causal=True,
+                                         local_window=200),
     "mask_fma_scale_0p1_bf16_d64": dict(seed=66, batch=2, heads=2, kv_heads=2, sq=140, sk=300,
                                         dim=64, dtype="bf16", scale=0.1, mask="normal", mask_p=0.1,
                                         dead_rows=1),

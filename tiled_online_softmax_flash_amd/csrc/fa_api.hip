@@ -184,6 +184,14 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     else p.kfac = 1.4426950408889634f;                                        // x in natural units
     if (!std::isfinite(p.kfac) || !(p.kfac > 0.0f))
         return fail(FA_ERR_UNSUPPORTED, "softcap %g is too large for fp32 exponent scaling", (double)softcap);
+    {
+        // tanh y = y - y^3 / 3 + 2 y^5 / 15 + O(y^7), taken for |y| < 1/8 (y = cap_y * s)
+        const double k = p.kfac, c = p.cap_y;
+        p.tc_b1 = (float)(k * c);
+        p.tc_b3 = (float)(-k * c * c * c / 3.0);
+        p.tc_b5 = (float)(2.0 * k * c * c * c * c * c / 15.0);
+        p.tc_slim = c != 0.0 ? (float)(1.0 / (8.0 * std::fabs(c))) : INFINITY;
+    }
     // Masked bf16 head-dim-64 ring launches whose scale is a power of two in [2^-20, 1] (the
     // default 1/8 included): the kernel multiplies Q by the scale, which only moves bf16 exponents
     // (exact above 2^-123 in magnitude), and starts the Q.K products from the mask values.

@@ -157,6 +157,11 @@ fwd16_ring_kernel(const FwdParams p) {
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
     const float cap_z = p.cap_y * kTanhZ;   // dot product -> argument of tanh_*_z
+    // Identity-form softcap without a mask: the speculative softmax of a full half-tile takes the
+    // base-2 exponent k tanh(c s) straight from the dot product s as the odd polynomial
+    // s (b1 + s^2 (b3 + b5 s^2)) (the series of tanh, valid while |s| < s_lim); a lane with a
+    // larger |s| sends its row through fix_up, which forms the scores exactly.
+    constexpr bool POLY = SOFTCAP == 2 && !MASKED;
     const scalar* __restrict__ qg = (const scalar*)p.q;
 
     // ---- DMA source offsets: DMA op i of a tile writes physical 16-byte chunks [64 i, 64 i + 64)
@@ -594,13 +599,22 @@ fwd16_ring_kernel(const FwdParams p) {
         bool moved;   // EXACT: the running maximum moved
         bool redo;    // speculative: the row needs fix_up
         bool big;     // speculative, masked: the row's exponent offset is too large to fold in
+        float smax;   // speculative, POLY: largest |s| of the lane's scores
     };
     auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, u32x4 (&pf)[2],
                              SoftmaxState& st, auto exact_c) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
         constexpr bool EXACT = decltype(exact_c)::value;
         constexpr int rb = decltype(rb_c)::value;
-        if (ph == 0 || ph == 1) {
+        constexpr bool SPEC_POLY = POLY && FULL && !EXACT;
+        if (SPEC_POLY && (ph == 0 || ph == 1)) {
+            // the scores stay raw dot products; only their range is checked
+            if (ph == 0) st.smax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                st.smax = __builtin_fmaxf(__builtin_fmaxf(st.smax, __builtin_fabsf(sc[8 * ph + e])),
+                                          __builtin_fabsf(sc[8 * ph + e + 1]));
+        } else if (ph == 0 || ph == 1) {
             if (ph == 0) {
                 st.mt = neg_inf();
                 if constexpr (!FULL) {
@@ -668,7 +682,12 @@ fwd16_ring_kernel(const FwdParams p) {
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * (ph - 3) + e;
                 // (the scores stay in sc for fix_up)
-                st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
+                if constexpr (SPEC_POLY) {
+                    const float sv = sc[v], s2 = sv * sv;
+                    st.pt[e] = exp2_hw(__builtin_fmaf(sv, __builtin_fmaf(s2, __builtin_fmaf(s2, p.tc_b5, p.tc_b3), p.tc_b1), st.nmk));
+                } else {
+                    st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
+                }
             }
         } else if (ph == 7 && !EXACT) {
             set_pair(pf, 12, st.pt[0], st.pt[1]);
@@ -678,6 +697,7 @@ fwd16_ring_kernel(const FwdParams p) {
             l_run[rb] += lsum;
             st.redo = !(lsum <= kSpecBound) || m_run[rb] == neg_inf();
             if constexpr (MASKED) st.redo = st.redo || st.big;
+            if constexpr (SPEC_POLY) st.redo = st.redo || !(st.smax < p.tc_slim);
         } else if (ph == 2) {
             const float mt = half_swap_max(st.mt);
             const bool need = mt > m_run[rb] + th_x;
@@ -712,8 +732,16 @@ fwd16_ring_kernel(const FwdParams p) {
     // it if it is larger, and recompute the row's weights as 2^((x - m) k) with the difference
     // formed before scaling (safe for scores near the float range's end, as in the exact form);
     // O and the denominator are scaled by 2^((m_old - m) k), or by 0 for a row that had no key.
-    auto fix_up = [&](auto rb_c, f32x16& sc, u32x4 (&pf)[2], SoftmaxState& st) __attribute__((always_inline)) {
+    auto fix_up = [&](auto full_c, auto rb_c, f32x16& sc, u32x4 (&pf)[2], SoftmaxState& st) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_c)::value;
+        if constexpr (POLY && decltype(full_c)::value) {
+            // the speculative pass left raw dot products: form the capped scores exactly
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float z = sc[v] * cap_z;
+                sc[v] = __builtin_fabsf(z) < kTanhSeriesMaxZ ? tanh_series_z(z) : tanh_identity_z(z);
+            }
+        }
         float am = neg_inf();
 #pragma unroll
         for (int v = 0; v < 16; ++v) am = __builtin_fmaxf(am, sc[v]);
@@ -904,7 +932,7 @@ fwd16_ring_kernel(const FwdParams p) {
             } else {
                 static_for<0, RB>([&](auto rb_c) __attribute__((always_inline)) {
                     constexpr int rb = decltype(rb_c)::value;
-                    if (wave_any(st[rb].redo)) fix_up(rb_c, s_cur[rb], p_cur[rb], st[rb]);
+                    if (wave_any(st[rb].redo)) fix_up(full_c, rb_c, s_cur[rb], p_cur[rb], st[rb]);
                 });
             }
         }

@@ -54,6 +54,9 @@ struct FwdParams {
     float softcap;
     float cap_y;                 // scale / softcap: dot product -> tanh argument
     float kfac;                  // log2(e) per unit of the tracked score
+    // softcap without a mask: the base-2 exponent kfac * tanh(cap_y * s) of a dot product s as
+    // s (tc_b1 + s^2 (tc_b3 + tc_b5 s^2)), the odd series of tanh to fifth order, for |s| < tc_slim
+    float tc_b1, tc_b3, tc_b5, tc_slim;
     int64_t kv_capacity;
     int64_t o_stride_b, o_stride_h, o_stride_i;  // output strides in elements
 };
