@@ -71,7 +71,7 @@ int dsa_check_args(const void* query, const void* key, const void* weights, cons
                    size_t workspace_bytes);
 
 /* Workspace bytes dsa_index_select needs: 4 per (batch, query row, key position) cell (the
- * cells' order keys, first), then for every query row 8224 bytes of histogram and counters and
+ * cells' order keys, first), then for every query row 16416 bytes of histograms and counters and
  * 4 bytes per 2048 key positions, then 8 bytes per cell (threshold candidates and positions); 0 when key_seq or batch * q_seq is 0, for
  * negative sizes or on overflow.  Host only. */
 size_t dsa_index_select_workspace_bytes(int batch, int q_seq, int key_seq);

@@ -233,10 +233,10 @@ def dsa_status(**over):
 
 
 def test_dsa_workspace_bytes():
-    # keys (4 B per cell), then per row 2056 words and one word per 2048-position chunk, then
+    # keys (4 B per cell), then per row 4104 words and one word per 2048-position chunk, then
     # 8 B per cell (candidates)
-    assert fa.dsa_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 12 + 6 * 2056 * 4 + 6 * 1 * 4
-    assert fa.dsa_workspace_bytes(1, 2, 4097) == 2 * 4097 * 12 + 2 * 2056 * 4 + 2 * 3 * 4
+    assert fa.dsa_workspace_bytes(2, 3, 1000) == 2 * 3 * 1000 * 12 + 6 * 4104 * 4 + 6 * 1 * 4
+    assert fa.dsa_workspace_bytes(1, 2, 4097) == 2 * 4097 * 12 + 2 * 4104 * 4 + 2 * 3 * 4
     assert fa.dsa_workspace_bytes(2, 3, 0) == 0
     assert fa.dsa_workspace_bytes(-1, 3, 10) == 0
     assert fa.dsa_workspace_bytes(2**30, 2**30, 2**30) == 0

@@ -24,7 +24,7 @@ struct DsaParams {
 // Selection chunks and per-row workspace words (see dsa_select.hip): the workspace holds the
 // keys (4 bytes per cell), then kAuxInts words per row, then one word per chunk of
 // kSelChunkKeys positions of every row, then two words per cell (candidate keys and positions).
-constexpr int kAuxInts = 2056;
+constexpr int kAuxInts = 4104;
 constexpr int kSelChunkKeys = 2048;
 
 // dtype 0 f32, 1 f16, 2 bf16; head_dim <= 128.  Enqueues the scoring kernel (when key_seq > 0)

@@ -20,14 +20,16 @@
 //         its allowed count);
 //       dsa_cand_kernel: every chunk reads the finished histogram back, finds the threshold's
 //         top digit d0, stores its count of keys with a larger top digit, and appends its keys
-//         with top digit d0 (the candidates, with their positions) to the row's list;
-//       dsa_write_kernel: every chunk finds the threshold's other two digits among the row's
-//         candidates by itself, and from the stored counts and the candidates' positions the
-//         keys above and equal to the threshold in the chunks before it; it then places its
-//         winners: every key above the threshold, and the first keys equal to it, as many as
-//         the rank left over (ties go to the lower position), in ascending position order.
-//     The rest of the row is -1.  The scoring kernel clears the row's histogram and counters, so
-//     a call needs no memset.
+//         with top digit d0 (the candidates, with their positions) to the row's list, counting
+//         their second digits into the row's second histogram;
+//       dsa_write_kernel: every chunk finds the threshold's second digit from that histogram and
+//         its third among the row's candidates by itself, and from the stored counts and the
+//         candidates' positions the keys above and equal to the threshold in the chunks before
+//         it; it then places its winners: every key above the threshold, and the first keys
+//         equal to it, as many as the rank left over (ties go to the lower position), in
+//         ascending position order.
+//     The rest of the row is -1.  The scoring kernel clears the row's histograms and counters,
+//     so a call needs no memset.
 // The kernels compute in float32 like the page's; the selection is integer-exact.
 #include <hip/hip_runtime.h>
 
@@ -243,14 +245,16 @@ constexpr int kKeysPerThread = kSelChunk / kSelThreads;
 // The threshold key is found by digits of 11, 11 and 10 bits (most significant first).  Per-row
 // auxiliary words after the keys in the workspace (kAuxInts per row): the histogram of the top
 // digit (2048 words), then the allowed count, the candidate count, and the row's top digit,
-// the rank left among the candidates and keep, as the candidate kernel found them.  Then per
+// the rank left among the candidates and keep, as the candidate kernel found them, and from
+// word kAuxH1 the histogram of the candidates' second digit (2048 words).  Then per
 // chunk of every row: its keys with a larger top digit.  Then per row up to key_seq candidates
 // (keys whose top digit is the threshold's) and, after them, their positions.
 constexpr int kMaxBins = 2048;
 __host__ __device__ constexpr int pass_bits(int q) { return q < 2 ? 11 : 10; }
 __host__ __device__ constexpr int pass_shift(int q) { return q == 0 ? 21 : (q == 1 ? 10 : 0); }
 constexpr int kAuxAllowed = 2048, kAuxCand = 2049, kAuxD0 = 2050, kAuxRank = 2051, kAuxKeep = 2052;
-static_assert(kAuxKeep < kAuxInts, "per-row words");
+constexpr int kAuxH1 = 2056;
+static_assert(kAuxKeep < kAuxH1 && kAuxH1 + (1 << 11) <= kAuxInts, "per-row words");
 
 __host__ __device__ __forceinline__ int64_t sel_chunks(int64_t T) { return (T + kSelChunk - 1) / kSelChunk; }
 
@@ -260,17 +264,16 @@ __host__ __device__ __forceinline__ int64_t sel_chunks(int64_t T) { return (T + 
 // nb-1-DPT*i down to nb-DPT*(i+1); a prefix over the threads finds the thread whose run holds
 // the crossing, which walks its digits.  All 256 threads call it (barriers); every thread gets
 // the result.
-__device__ __forceinline__ int find_digit(const int* hist, int nb, int rank, int* wsum, int* pick, int* above) {
+// find_digit_counts takes thread i's counts c[j] = hist[nb - 1 - DPT*i - j] (0 for j >= DPT)
+// already loaded.
+__device__ __forceinline__ int find_digit_counts(const int (&c)[kMaxBins / kSelThreads], int nb, int rank, int* wsum,
+                                                 int* pick, int* above) {
     const int tid = threadIdx.x;
     const int dpt = nb / kSelThreads;
     const int hi = nb - 1 - dpt * tid;
-    int c[kMaxBins / kSelThreads];
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxBins / kSelThreads; ++j) {
-        c[j] = j < dpt ? hist[hi - j] : 0;
-        cnt += c[j];
-    }
+    for (int j = 0; j < kMaxBins / kSelThreads; ++j) cnt += c[j];
     int total;
     const int cum = block_inclusive_sum<kSelThreads>(cnt, wsum, &total);
     if (cum >= rank && cum - cnt < rank) {
@@ -289,6 +292,14 @@ __device__ __forceinline__ int find_digit(const int* hist, int nb, int rank, int
     *above = pick[1];
     __syncthreads();
     return digit;
+}
+__device__ __forceinline__ int find_digit(const int* hist, int nb, int rank, int* wsum, int* pick, int* above) {
+    const int dpt = nb / kSelThreads;
+    const int hi = nb - 1 - dpt * (int)threadIdx.x;
+    int c[kMaxBins / kSelThreads];
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kSelThreads; ++j) c[j] = j < dpt ? hist[hi - j] : 0;
+    return find_digit_counts(c, nb, rank, wsum, pick, above);
 }
 
 // Histogram of the top digit over one chunk, added into the row's; the allowed positions are
@@ -334,8 +345,9 @@ __global__ void __launch_bounds__(kSelThreads) dsa_hist_kernel(const DsaParams p
 // Each chunk finds, from the row's finished histogram, keep, the top digit d0 of the keep-th
 // largest key and the rank left among the keys with that digit; stores its own count of keys
 // with a larger top digit; and appends its keys with top digit d0 (the candidates) and their
-// positions to the row's list.  Chunk 0 records d0, the rank and keep.  The slots past keep are
-// set to -1 here (spread over the row's chunks).
+// positions to the row's list, and counts their second digits into the row's second histogram.
+// Chunk 0 records d0, the rank and keep.  The slots past keep are set to -1 here (spread over the
+// row's chunks).
 __global__ void __launch_bounds__(kSelThreads) dsa_cand_kernel(const DsaParams p) {
     __shared__ int wsum[kSelThreads / 64];
     __shared__ int w2[kSelThreads / 64][2];
@@ -387,6 +399,7 @@ __global__ void __launch_bounds__(kSelThreads) dsa_cand_kernel(const DsaParams p
             cand_key[at] = (int)k8[j];
             cand_pos[at] = (int)(t0 + j);
             ++at;
+            atomicAdd(&aux[kAuxH1 + ((k8[j] >> pass_shift(1)) & ((1u << pass_bits(1)) - 1u))], 1);
         }
     }
 }
@@ -419,7 +432,6 @@ __device__ __forceinline__ int cand_digit(KeyPtr cand_key, int n, uint32_t prefi
 constexpr int kCandLds = 2048;   // candidates the write kernel keeps in LDS (8 per thread)
 
 __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams p) {
-    __shared__ int hist[kMaxBins];
     __shared__ int hist2[1 << pass_bits(2)];
     __shared__ uint32_t ck[kCandLds];
     __shared__ int cp[kCandLds];
@@ -452,6 +464,12 @@ __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams 
         ckr[j] = i < T ? (uint32_t)cand_key[i] : 0u;
         cpr[j] = i < T ? cand_pos[i] : 0;
     }
+    // the candidates' second-digit histogram, this thread's run of find_digit_counts
+    constexpr int DPT1 = (1 << pass_bits(1)) / kSelThreads;
+    int c1[kMaxBins / kSelThreads];
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kSelThreads; ++j)
+        c1[j] = j < DPT1 ? aux[kAuxH1 + (1 << pass_bits(1)) - 1 - DPT1 * tid - j] : 0;
     int gt_b = 0, eq_b = 0;   // keys above (then also equal to) the threshold before this chunk
     for (int64_t c = tid; c < ch; c += kSelThreads) gt_b += p.counts[row * nch + c];
     const int64_t allowed = aux[kAuxAllowed];
@@ -466,16 +484,15 @@ __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams 
         ck[j * kSelThreads + tid] = ckr[j];
         cp[j * kSelThreads + tid] = cpr[j];
     }
-    for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
     for (int i = tid; i < (1 << pass_bits(2)); i += kSelThreads) hist2[i] = 0;
     __syncthreads();
     // the threshold's other two digits, and the candidates above and equal to it before this chunk
     int above;
     uint32_t thr;
     const int64_t lim = ch * kSelChunk;
+    prefix |= (uint32_t)find_digit_counts(c1, 1 << pass_bits(1), rank, wsum, pick, &above) << pass_shift(1);
+    rank -= above;
     if (in_lds) {
-        prefix |= (uint32_t)cand_digit<1>(ck, n, prefix, rank, hist, wsum, pick, &above) << pass_shift(1);
-        rank -= above;
         thr = prefix | (uint32_t)cand_digit<2>(ck, n, prefix, rank, hist2, wsum, pick, &above);
         for (int i = tid; i < n; i += kSelThreads) {
             if (cp[i] < lim) {
@@ -484,8 +501,6 @@ __global__ void __launch_bounds__(kSelThreads) dsa_write_kernel(const DsaParams 
             }
         }
     } else {
-        prefix |= (uint32_t)cand_digit<1>(cand_key, n, prefix, rank, hist, wsum, pick, &above) << pass_shift(1);
-        rank -= above;
         thr = prefix | (uint32_t)cand_digit<2>(cand_key, n, prefix, rank, hist2, wsum, pick, &above);
         for (int i = tid; i < n; i += kSelThreads) {
             if (cand_pos[i] < lim) {
