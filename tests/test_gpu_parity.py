@@ -207,6 +207,13 @@ EDGE = {
     "softcap_series_edge_bf16_d64": dict(seed=68, batch=2, heads=4, kv_heads=1, sq=280, sk=520,
                                          dim=64, dtype="bf16", softcap=4.0, causal=True,
                                          local_window=200),
+    # the softcap's polynomial exponent with a negative scale (odd coefficients change sign) and
+    # with a zero scale (every score 0: uniform weights)
+    "softcap_negative_scale_f16_d128": dict(seed=69, batch=2, heads=2, kv_heads=1, sq=150, sk=260,
+                                            dim=128, dtype="f16", softcap=6.0, scale=-0.3,
+                                            causal=True),
+    "softcap_zero_scale_bf16_d64": dict(seed=70, batch=1, heads=3, kv_heads=3, sq=90, sk=200,
+                                        dim=64, dtype="bf16", softcap=20.0, scale=0.0),
     "mask_fma_scale_0p1_bf16_d64": dict(seed=66, batch=2, heads=2, kv_heads=2, sq=140, sk=300,
                                         dim=64, dtype="bf16", scale=0.1, mask="normal", mask_p=0.1,
                                         dead_rows=1),

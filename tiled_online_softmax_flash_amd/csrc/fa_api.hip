@@ -194,7 +194,8 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
     }
     // Masked bf16 head-dim-64 ring launches whose scale is a power of two in [2^-20, 1] (the
     // default 1/8 included): the kernel multiplies Q by the scale, which only moves bf16 exponents
-    // (exact above 2^-123 in magnitude), and starts the Q.K products from the mask values.
+    // (exact unless a scaled value falls below 2^-126, the smallest normal bf16), and starts the
+    // Q.K products from the mask values.
     int scale_exp = 0;
     const float scale_mant = std::frexp(scale, &scale_exp);
     p.mask_in_acc = (plan->ring && dtype == FA_DTYPE_BF16 && mask_planes > 0 && !has_cap && dim == 64 &&
