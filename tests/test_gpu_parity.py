@@ -191,13 +191,13 @@ EDGE = {
                                            mask_dtype="bf16"),
     "mask_extreme_fp32": dict(seed=62, batch=1, heads=2, kv_heads=1, sq=50, sk=130, dim=64,
                               dtype="f32", mask="extreme", mask_p=0.05),
-    # masked bf16 head dim 64 with a power-of-two scale: Q takes the scale and the Q.K products
-    # start from the mask values (fp32 and 16-bit masks); a scale that is not a power of two
-    # keeps the per-score multiply-add
+    # masked bf16 head dim 64 with a power-of-two scale and an fp32 mask: Q takes the scale and
+    # the Q.K products start from the mask values; a 16-bit mask, or a scale that is not a power
+    # of two, keeps the per-score multiply-add
     "mask_acc_scale_one_bf16_d64": dict(seed=64, batch=2, heads=3, kv_heads=3, sq=200, sk=330,
                                         dim=64, dtype="bf16", scale=1.0, amp=0.3, mask="normal",
                                         mask_p=0.1, dead_rows=2),
-    "mask_acc_scale_2m5_bf16mask": dict(seed=65, batch=2, heads=2, kv_heads=1, sq=150, sk=260,
+    "mask_pow2_scale_bf16mask": dict(seed=65, batch=2, heads=2, kv_heads=1, sq=150, sk=260,
                                         dim=64, dtype="bf16", scale=2.0 ** -5, mask="ramp",
                                         mask_ramp=0.25, mask_p=0.1, mask_dtype="bf16", causal=True),
     # softcaps at which many scores straddle |s / c| = 1/8, where the speculative softmax's

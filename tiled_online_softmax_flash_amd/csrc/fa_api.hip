@@ -192,14 +192,14 @@ int validate(const void* q, const void* k, const void* v, const void* mask, cons
         p.tc_b5 = (float)(2.0 * k * c * c * c * c * c / 15.0);
         p.tc_slim = c != 0.0 ? (float)(1.0 / (8.0 * std::fabs(c))) : INFINITY;
     }
-    // Masked bf16 head-dim-64 ring launches whose scale is a power of two in [2^-20, 1] (the
-    // default 1/8 included): the kernel multiplies Q by the scale, which only moves bf16 exponents
+    // Ring launches with bf16 inputs, head dim 64, an fp32 mask and a scale that is a power of two
+    // in [2^-20, 1] (the default 1/8 included): the kernel multiplies Q by the scale, which only moves bf16 exponents
     // (exact unless a scaled value falls below 2^-126, the smallest normal bf16), and starts the
     // Q.K products from the mask values.
     int scale_exp = 0;
     const float scale_mant = std::frexp(scale, &scale_exp);
-    p.mask_in_acc = (plan->ring && dtype == FA_DTYPE_BF16 && mask_planes > 0 && !has_cap && dim == 64 &&
-                     scale_mant == 0.5f && scale_exp >= -19 && scale_exp <= 1) ? 1 : 0;
+    p.mask_in_acc = (plan->ring && dtype == FA_DTYPE_BF16 && mask_planes > 0 && mask_dtype == FA_DTYPE_F32 &&
+                     !has_cap && dim == 64 && scale_mant == 0.5f && scale_exp >= -19 && scale_exp <= 1) ? 1 : 0;
     plan->dp = plan->wide ? 384 : (dim + 31) / 32 * 32;
     plan->grid = (int)grid;
     return FA_OK;

@@ -116,9 +116,11 @@ fwd16_ring_kernel(const FwdParams p) {
     // RAW with a mask: the scale is a power of two that Q takes exactly (multiplied in once per
     // item), and each half-tile's Q.K products start from its mask values instead of zero, so
     // the accumulators hold scale * (Q.K) + mask and the scores need no per-element
-    // multiply-add.  Needs the mask a block before its softmax: the head-dim-64 schedule.
+    // multiply-add.  The second block of a step then reads the mask of the next step's first
+    // half-tile: only the LDS-staged fp32 mask has it in registers by then (read out at the end
+    // of the step before); the 16-bit masks' loads of that step are still in flight.
     constexpr bool MASK_ACC = MASKED && RAW;
-    static_assert(!MASK_ACC || (MASK_AHEAD && SOFTCAP == 0), "mask accumulation needs the mask-ahead schedule");
+    static_assert(!MASK_ACC || (MASK_LDS && SOFTCAP == 0), "mask accumulation needs the LDS-staged mask");
     constexpr int MSK_WAVE = 2 * 32 * 128;   // one step's fp32 mask of a wave: 2 half-tiles x 32 rows x 128 B
     // LDS operand reads kept in flight ahead of their MFMA; the masked head-dim-128 variants hold
     // a step's mask values as well, and the head-dim-128 variants with a softcap or a scale
@@ -1222,12 +1224,10 @@ hipError_t launch_ring_dp(const FwdParams& p, int grid, int maskk, bool softcap,
         return identity ? launch_ring_one<Tr, DP, kMaskNone, 2, false>(p, grid, s)
                         : launch_ring_one<Tr, DP, kMaskNone, 1, false>(p, grid, s);
     }
-    // (mask accumulation: bf16 only, whose exponent range lets Q take the scale exactly)
+    // (mask accumulation: bf16 only, whose exponent range lets Q take the scale exactly, with
+    // the LDS-staged fp32 mask)
     if constexpr (DP == 64 && std::is_same<Tr, TraitsBF16>::value) {
-        if (p.mask_in_acc) {
-            if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, true>(p, grid, s);
-            if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, true>(p, grid, s);
-        }
+        if (p.mask_in_acc && maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, true>(p, grid, s);
     }
     if (maskk == kMaskF32) return launch_ring_one<Tr, DP, kMaskF32, 0, false>(p, grid, s);
     if (maskk == kMaskT) return launch_ring_one<Tr, DP, kMaskT, 0, false>(p, grid, s);
