@@ -159,8 +159,8 @@ fwd16_ring_kernel(const FwdParams p) {
     const float kfac = p.kfac;
     const float th_x = kRescaleLog2 / kfac;
     const float cap_z = p.cap_y * kTanhZ;   // dot product -> argument of tanh_*_z
-    // Identity-form softcap without a mask: the speculative softmax of a full half-tile takes the
-    // base-2 exponent k tanh(c s) straight from the dot product s as the odd polynomial
+    // Identity-form softcap without a mask: the speculative softmax (full and partial half-tiles)
+    // takes the base-2 exponent k tanh(c s) straight from the dot product s as the odd polynomial
     // s (b1 + s^2 (b3 + b5 s^2)) (the series of tanh, valid while |s| < s_lim); a lane with a
     // larger |s| sends its row through fix_up, which forms the scores exactly.
     constexpr bool POLY = SOFTCAP == 2 && !MASKED;
@@ -608,10 +608,23 @@ fwd16_ring_kernel(const FwdParams p) {
         constexpr bool FULL = decltype(full_c)::value;
         constexpr bool EXACT = decltype(exact_c)::value;
         constexpr int rb = decltype(rb_c)::value;
-        constexpr bool SPEC_POLY = POLY && FULL && !EXACT;
+        constexpr bool SPEC_POLY = POLY && !EXACT;
+        // bit v of keep: element v (key base + v) lies in the row's key range
+        auto set_keep = [&]() __attribute__((always_inline)) {
+            const int base = half_k0(u) + 16 * hh;
+            const int lo_rel = my_lo32[rb] - base;
+            const int hi_rel = my_hi32[rb] - base;
+            const uint32_t below_hi = hi_rel < 0 ? 0u : (hi_rel >= 15 ? 0xffffu : (2u << hi_rel) - 1u);
+            const uint32_t below_lo = lo_rel <= 0 ? 0u : (lo_rel >= 16 ? 0xffffu : (1u << lo_rel) - 1u);
+            st.keep = below_hi & ~below_lo;
+        };
         if (SPEC_POLY && (ph == 0 || ph == 1)) {
-            // the scores stay raw dot products; only their range is checked
-            if (ph == 0) st.smax = 0.0f;
+            // the scores stay raw dot products; only their range is checked (masked elements
+            // included: a large one costs a redo, not a wrong result)
+            if (ph == 0) {
+                st.smax = 0.0f;
+                if constexpr (!FULL) set_keep();
+            }
 #pragma unroll
             for (int e = 0; e < 8; e += 2)
                 st.smax = __builtin_fmaxf(__builtin_fmaxf(st.smax, __builtin_fabsf(sc[8 * ph + e])),
@@ -619,15 +632,7 @@ fwd16_ring_kernel(const FwdParams p) {
         } else if (ph == 0 || ph == 1) {
             if (ph == 0) {
                 st.mt = neg_inf();
-                if constexpr (!FULL) {
-                    // bit v of keep: element v (key base + v) lies in the row's key range
-                    const int base = half_k0(u) + 16 * hh;
-                    const int lo_rel = my_lo32[rb] - base;
-                    const int hi_rel = my_hi32[rb] - base;
-                    const uint32_t below_hi = hi_rel < 0 ? 0u : (hi_rel >= 15 ? 0xffffu : (2u << hi_rel) - 1u);
-                    const uint32_t below_lo = lo_rel <= 0 ? 0u : (lo_rel >= 16 ? 0xffffu : (1u << lo_rel) - 1u);
-                    st.keep = below_hi & ~below_lo;
-                }
+                if constexpr (!FULL) set_keep();
             }
             // identity-form softcap: the eight tanh arguments of the phase take the series when
             // all of the wave's are below 1/8 (no transcendental), else the identity
@@ -686,7 +691,13 @@ fwd16_ring_kernel(const FwdParams p) {
                 // (the scores stay in sc for fix_up)
                 if constexpr (SPEC_POLY) {
                     const float sv = sc[v], s2 = sv * sv;
-                    st.pt[e] = exp2_hw(__builtin_fmaf(sv, __builtin_fmaf(s2, __builtin_fmaf(s2, p.tc_b5, p.tc_b3), p.tc_b1), st.nmk));
+                    float ex = __builtin_fmaf(sv, __builtin_fmaf(s2, __builtin_fmaf(s2, p.tc_b5, p.tc_b3), p.tc_b1), st.nmk);
+                    if constexpr (!FULL) {
+                        // masked elements get the exponent -inf, weight 0
+                        const uint32_t sel = (uint32_t)((int32_t)(st.keep << (31 - v)) >> 31);
+                        ex = __uint_as_float((sel & __float_as_uint(ex)) | (~sel & 0xff800000u));
+                    }
+                    st.pt[e] = exp2_hw(ex);
                 } else {
                     st.pt[e] = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
                 }
@@ -736,12 +747,17 @@ fwd16_ring_kernel(const FwdParams p) {
     // O and the denominator are scaled by 2^((m_old - m) k), or by 0 for a row that had no key.
     auto fix_up = [&](auto full_c, auto rb_c, f32x16& sc, u32x4 (&pf)[2], SoftmaxState& st) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_c)::value;
-        if constexpr (POLY && decltype(full_c)::value) {
-            // the speculative pass left raw dot products: form the capped scores exactly
+        if constexpr (POLY) {
+            // the speculative pass left raw dot products: form the capped scores exactly (and
+            // -inf for masked elements of a partial half-tile)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float z = sc[v] * cap_z;
-                sc[v] = __builtin_fabsf(z) < kTanhSeriesMaxZ ? tanh_series_z(z) : tanh_identity_z(z);
+                float x = __builtin_fabsf(z) < kTanhSeriesMaxZ ? tanh_series_z(z) : tanh_identity_z(z);
+                if constexpr (!decltype(full_c)::value) {
+                    if (!((st.keep >> v) & 1u)) x = neg_inf();
+                }
+                sc[v] = x;
             }
         }
         float am = neg_inf();
