@@ -602,6 +602,7 @@ fwd16_ring_kernel(const FwdParams p) {
         bool redo;    // speculative: the row needs fix_up
         bool big;     // speculative, masked: the row's exponent offset is too large to fold in
         float smax;   // speculative, POLY: largest |s| of the lane's scores
+        bool fb;      // exact, POLY: some score of the wave is out of the series' range
     };
     auto softmax_phase = [&](auto full_c, auto rb_c, int ph, int u, f32x16& sc, const MaskH& mh, u32x4 (&pf)[2],
                              SoftmaxState& st, auto exact_c) __attribute__((always_inline)) {
@@ -609,6 +610,10 @@ fwd16_ring_kernel(const FwdParams p) {
         constexpr bool EXACT = decltype(exact_c)::value;
         constexpr int rb = decltype(rb_c)::value;
         constexpr bool SPEC_POLY = POLY && !EXACT;
+        // exact softmax with POLY: the scores become base-2 exponents k x (the polynomial, or the
+        // exact forms times k when some score of the wave is out of the series' range), and the
+        // running maximum is taken over them
+        constexpr bool EXACT_POLY = POLY && EXACT;
         // bit v of keep: element v (key base + v) lies in the row's key range
         auto set_keep = [&]() __attribute__((always_inline)) {
             const int base = half_k0(u) + 16 * hh;
@@ -629,6 +634,41 @@ fwd16_ring_kernel(const FwdParams p) {
             for (int e = 0; e < 8; e += 2)
                 st.smax = __builtin_fmaxf(__builtin_fmaxf(st.smax, __builtin_fabsf(sc[8 * ph + e])),
                                           __builtin_fabsf(sc[8 * ph + e + 1]));
+        } else if (EXACT_POLY && (ph == 0 || ph == 1)) {
+            if (ph == 0) {
+                st.mt = neg_inf();
+                if constexpr (!FULL) set_keep();
+                float am = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 16; e += 2)
+                    am = __builtin_fmaxf(__builtin_fmaxf(am, __builtin_fabsf(sc[e])), __builtin_fabsf(sc[e + 1]));
+                st.fb = wave_any(!(am < p.tc_slim));
+            }
+            float ex[8];
+            if (!st.fb) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = sc[8 * ph + e], s2 = sv * sv;
+                    ex[e] = sv * __builtin_fmaf(s2, __builtin_fmaf(s2, p.tc_b5, p.tc_b3), p.tc_b1);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float z = sc[8 * ph + e] * cap_z;
+                    ex[e] = (__builtin_fabsf(z) < kTanhSeriesMaxZ ? tanh_series_z(z) : tanh_identity_z(z)) * kfac;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int v = 8 * ph + e;
+                float x = ex[e];
+                if constexpr (!FULL) {
+                    const uint32_t sel = (uint32_t)((int32_t)(st.keep << (31 - v)) >> 31);
+                    x = __uint_as_float((sel & __float_as_uint(x)) | (~sel & 0xff800000u));
+                }
+                sc[v] = x;
+                st.mt = __builtin_fmaxf(st.mt, x);
+            }
         } else if (ph == 0 || ph == 1) {
             if (ph == 0) {
                 st.mt = neg_inf();
@@ -712,7 +752,10 @@ fwd16_ring_kernel(const FwdParams p) {
             if constexpr (MASKED) st.redo = st.redo || st.big;
             if constexpr (SPEC_POLY) st.redo = st.redo || !(st.smax < p.tc_slim);
         } else if (ph == 2) {
-            const float mt = half_swap_max(st.mt);
+            // (EXACT_POLY: the maximum of exponents k x, back in units of x; th_x / kRescaleLog2 is
+            // 1 / k rounded once, kRescaleLog2 being a power of two)
+            static_assert(kRescaleLog2 == 8.0f, "th_x / kRescaleLog2 must be exact");
+            const float mt = EXACT_POLY ? half_swap_max(st.mt) * (th_x * (1.0f / kRescaleLog2)) : half_swap_max(st.mt);
             const bool need = mt > m_run[rb] + th_x;
             const float m_new = need ? mt : m_run[rb];
             st.alpha = need ? exp2_hw((m_run[rb] - m_new) * kfac) : 1.0f;
@@ -729,6 +772,7 @@ fwd16_ring_kernel(const FwdParams p) {
                 const int v = 4 * (ph - 3) + e;
                 float pv_;
                 if constexpr (SUB_FIRST) pv_ = exp2_hw((sc[v] - st.m_safe) * kfac);
+                else if constexpr (EXACT_POLY) pv_ = exp2_hw(sc[v] + st.nmk);   // (sc holds k x)
                 else pv_ = exp2_hw(__builtin_fmaf(sc[v], kfac, st.nmk));
                 sc[v] = pv_;   // probabilities overwrite the scores
             }
