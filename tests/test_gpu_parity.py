@@ -197,6 +197,9 @@ EDGE = {
     "mask_acc_scale_one_bf16_d64": dict(seed=64, batch=2, heads=3, kv_heads=3, sq=200, sk=330,
                                         dim=64, dtype="bf16", scale=1.0, amp=0.3, mask="normal",
                                         mask_p=0.1, dead_rows=2),
+    "mask_acc_per_head_planes_bf16_d64": dict(seed=71, batch=2, heads=3, kv_heads=3, sq=100,
+                                              sk=200, dim=64, dtype="bf16", mask="normal",
+                                              mask_planes=6, mask_p=0.1, dead_rows=1),
     "mask_pow2_scale_bf16mask": dict(seed=65, batch=2, heads=2, kv_heads=1, sq=150, sk=260,
                                         dim=64, dtype="bf16", scale=2.0 ** -5, mask="ramp",
                                         mask_ramp=0.25, mask_p=0.1, mask_dtype="bf16", causal=True),
